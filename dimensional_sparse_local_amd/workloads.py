@@ -1,0 +1,87 @@
+"""Workload descriptions and seeded synthetic inputs.
+
+Plain data and random-number generation only: nothing here computes any part
+of the attention.  Both the GPU library's binding and the CPU oracle read these
+descriptions, each translating them into its own descriptor.
+
+Pattern vocabulary (per grid dimension unless noted):
+
+* ``na``      window of ``window[d]`` positions centred on the query and shifted
+              inside the grid at the borders (neighbourhood attention);
+              optional ``stride`` (groups sharing one window) and ``dilation``.
+* ``sa``      the same window cut at the grid borders instead of shifted
+              (slide attention, zero padding).
+* ``band``    1-D only: keys in [x - left, x + right] cut at the ends
+              (bidirectional band; causal when right = 0).
+* ``blocked`` non-overlapping windows of ``window[d]`` positions.
+* ``sta``     sliding tile attention: tiles of ``tile[d]`` positions; the query's
+              tile attends ``window_tiles[d]`` whole tiles shifted inside.
+
+Orders: ``row_major``; ``tiled`` (tile by tile with tile extents ``tile``,
+row-major inside); ``hilbert`` (2-D square power-of-two grid; the pattern is
+then 1-D over the position along the curve).
+"""
+from __future__ import annotations
+
+import math
+
+# The five benchmark workloads.  Each gets its own seed (its index, 1-5).
+CONFIGS = {
+    "na2d_fp32": dict(
+        name="na2d_fp32", B=1, H=1, D=32, dtype="fp32", grid=[8, 8], order="row_major",
+        pattern=dict(kind="na", window=[3, 3]), seed=1,
+        note="2-D neighbourhood attention, 8x8 grid, 3x3 window clamped at borders"),
+    "na2d_bf16": dict(
+        name="na2d_bf16", B=2, H=8, D=64, dtype="bf16", grid=[64, 64], order="row_major",
+        pattern=dict(kind="na", window=[13, 13]), seed=2,
+        note="2-D neighbourhood attention, 64x64 grid, 13x13 window clamped at borders"),
+    "sta3d_bf16": dict(
+        name="sta3d_bf16", B=1, H=24, D=128, dtype="bf16", grid=[30, 48, 80], order="tiled",
+        tile=[6, 8, 8], pattern=dict(kind="sta", tile=[6, 8, 8], window_tiles=[3, 5, 7]),
+        seed=3,
+        note="3-D sliding tile attention, 30x48x80 grid, 6x8x8 tiles, 3x5x7-tile window"),
+    "hilbert_band_bf16": dict(
+        name="hilbert_band_bf16", B=4, H=12, D=64, dtype="bf16", grid=[128, 128],
+        order="hilbert", pattern=dict(kind="band", left=256, right=256), seed=4,
+        note="Hilbert slide attention, 128x128 grid, band radius 256 on the curve"),
+    "causal1d_bf16": dict(
+        name="causal1d_bf16", B=1, H=32, D=128, dtype="bf16", grid=[32768], order="row_major",
+        pattern=dict(kind="band", left=4095, right=0), seed=5,
+        note="1-D causal sliding window, 32768 tokens, 4096 keys including self"),
+}
+
+# The workload the benchmark times by default (the headline metric's config).
+HEADLINE = "sta3d_bf16"
+
+
+def num_tokens(w: dict) -> int:
+    return int(math.prod(int(g) for g in w["grid"]))
+
+
+def default_scale(w: dict) -> float:
+    return 1.0 / math.sqrt(int(w["D"]))
+
+
+def scaled(w: dict, **over) -> dict:
+    """A copy of workload w with fields replaced (e.g. fewer heads)."""
+    out = dict(w)
+    out.update(over)
+    return out
+
+
+def make_qkv(w: dict, device="cpu", seed: int | None = None):
+    """q, k, v ~ i.i.d. N(0, 1) of shape [B, H, N, D], drawn in that order in
+    fp32 from one generator seeded with the workload's seed, then rounded to
+    bf16 (round to nearest even) for bf16 workloads."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(w["seed"] if seed is None else seed))
+    shape = (int(w["B"]), int(w["H"]), num_tokens(w), int(w["D"]))
+    out = []
+    for _ in range(3):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if w["dtype"] == "bf16":
+            x = x.to(torch.bfloat16)
+        out.append(x)
+    return tuple(out)

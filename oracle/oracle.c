@@ -1,0 +1,405 @@
+/*
+ * Plain fp64 CPU oracle for N-dimensional local attention (forward only).
+ *
+ * TEST INFRASTRUCTURE ONLY: called from the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark, never from the product path.  It shares
+ * no code with the GPU library.
+ *
+ * Sources of each rule (pages as titled):
+ *  - softmax attention over a key set, and the causal / bidirectional local
+ *    neighbourhoods: "pi-Attention: Online Efficient Sparse Transformers for
+ *    Long-Context Modeling", Section 3.1 (Eqs. 1-3) and Section 3.2 (Eqs. 4-5);
+ *    invalid positions are excluded before the softmax (Appendix A, text after
+ *    Eq. 34).
+ *  - sliding tile attention (tiles share one window that moves tile by tile,
+ *    shifted inside the grid): "ENA: Efficient N-dimensional Attention",
+ *    reading notes ("What carries the argument", "Core claim").
+ *  - neighbourhood attention with the window shifted inside at the borders,
+ *    strided (grouped) and blocked windows: "Generalized Neighborhood
+ *    Attention", abstract.  The stride leader and the dilation sub-grid rule are
+ *    readings (the pages give only the names): a group of `stride` consecutive
+ *    positions shares the window of its middle position; dilation runs the
+ *    rule on the interleaved sub-grid of positions congruent to x.
+ *  - Hilbert reordering with windows / slides formed on the reordered 1-D
+ *    sequence, and the empty / partial / full tile classes:
+ *    "Hilbert-Guided Sparse Local Attention", "Methodology in Plain English"
+ *    and "Key Contributions".
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+static int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t orc_max_threads(void) {
+#ifdef _OPENMP
+    return (int32_t)omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int64_t orc_num_tokens(const orc_spec* s) {
+    int64_t n = 1;
+    for (int d = 0; d < s->ndim; ++d) n *= s->grid[d];
+    return n;
+}
+
+/* Grid extent of dimension d, 1 beyond ndim. */
+static int64_t extent(const orc_spec* s, int d) { return d < s->ndim ? s->grid[d] : 1; }
+
+/* ------------------------------------------------------------------------ */
+/* One-dimensional neighbourhood rules.                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Sliding window on an axis of length L at coordinate x (Eq. 5 of the
+   pi-Attention page generalised to a window of w positions that starts at
+   x - left).  With clamp the window is shifted to lie inside the axis (the
+   neighbourhood-attention border rule); without it the window is cut at the
+   axis ends (positions outside are invalid and dropped).  Stride: positions are
+   grouped `stride` at a time and each group uses the window of its middle
+   position.  Dilation: only positions congruent to x modulo `dil` take part,
+   and the rule runs in the coordinates of that sub-grid. */
+static int64_t window_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out) {
+    const int64_t dil = r->dil > 0 ? r->dil : 1;
+    const int64_t stride = r->stride > 0 ? r->stride : 1;
+    const int64_t g = x % dil;                 /* which interleaved sub-grid */
+    const int64_t xl = x / dil;                /* coordinate inside it */
+    const int64_t Lg = ceil_div(L - g, dil);   /* its length */
+    /* group leader; with stride 1 every position leads its own group */
+    const int64_t centre = (xl / stride) * stride + stride / 2;
+    int64_t lo, hi;
+    if (r->clamp) {
+        if (r->w >= Lg) {
+            lo = 0;
+            hi = Lg;
+        } else {
+            lo = imin(imax(centre - r->left, 0), Lg - r->w);
+            hi = lo + r->w;
+        }
+    } else {
+        lo = imax(centre - r->left, 0);
+        hi = imin(centre - r->left + r->w, Lg);
+    }
+    int64_t n = 0;
+    for (int64_t t = lo; t < hi; ++t) out[n++] = g + dil * t;
+    return n;
+}
+
+/* Non-overlapping windows of w positions; the last one may be shorter. */
+static int64_t blocked_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out) {
+    const int64_t lo = (x / r->w) * r->w;
+    const int64_t hi = imin(lo + r->w, L);
+    int64_t n = 0;
+    for (int64_t t = lo; t < hi; ++t) out[n++] = t;
+    return n;
+}
+
+/* Sliding tile attention on one axis: the axis is cut into tiles of `tile`
+   positions; the query's tile attends `wt` consecutive whole tiles centred on
+   it, shifted so that the window stays inside the axis. */
+static int64_t sta_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out) {
+    const int64_t T = ceil_div(L, r->tile);
+    const int64_t t = x / r->tile;
+    int64_t first, last; /* tile range [first, last) */
+    if (r->wt >= T) {
+        first = 0;
+        last = T;
+    } else {
+        first = imin(imax(t - r->wt / 2, 0), T - r->wt);
+        last = first + r->wt;
+    }
+    int64_t n = 0;
+    for (int64_t p = first * r->tile; p < imin(last * r->tile, L); ++p) out[n++] = p;
+    return n;
+}
+
+int64_t orc_rule_set(const orc_rule* r, int64_t len, int64_t x, int64_t* out) {
+    if (len <= 1) {
+        out[0] = 0;
+        return 1;
+    }
+    switch (r->kind) {
+        case ORC_WINDOW: return window_set(r, len, x, out);
+        case ORC_BLOCKED: return blocked_set(r, len, x, out);
+        case ORC_STA: return sta_set(r, len, x, out);
+        default: return -1;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Token orders.                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Emit the cells of a size x size block from corner (r, c), travelling first
+   along direction u and turning into the block along direction v.  The block
+   is split into four quadrants visited in a U: the start quadrant (whose own
+   curve is transposed so that it ends next to the second one), the quadrant
+   one half-step along v, the one diagonal to the start, and the one one
+   half-step along u (whose curve is reversed and transposed so that it ends at
+   the block's end corner, (size-1) steps along u from the start). */
+static void hilbert_rec(int64_t n, int64_t size, int64_t r, int64_t c, int64_t ur, int64_t uc,
+                        int64_t vr, int64_t vc, int64_t* perm, int64_t* k) {
+    if (size == 1) {
+        perm[(*k)++] = r * n + c;
+        return;
+    }
+    const int64_t h = size / 2;
+    hilbert_rec(n, h, r, c, vr, vc, ur, uc, perm, k);
+    hilbert_rec(n, h, r + h * vr, c + h * vc, ur, uc, vr, vc, perm, k);
+    hilbert_rec(n, h, r + h * vr + h * ur, c + h * vc + h * uc, ur, uc, vr, vc, perm, k);
+    hilbert_rec(n, h, r + (h - 1) * vr + (2 * h - 1) * ur, c + (h - 1) * vc + (2 * h - 1) * uc,
+                -vr, -vc, -ur, -uc, perm, k);
+}
+
+int orc_hilbert(int64_t n, int64_t* perm) {
+    if (n < 1 || (n & (n - 1)) != 0) return -1;
+    int64_t k = 0;
+    /* Start at (row 0, col 0), end at (row 0, col n-1): u points along the
+       columns, v down the rows. */
+    hilbert_rec(n, n, 0, 0, 0, 1, 1, 0, perm, &k);
+    return 0;
+}
+
+int orc_order(const orc_spec* s, int64_t* perm) {
+    const int64_t N = orc_num_tokens(s);
+    if (s->order == ORC_ORDER_ROW_MAJOR) {
+        for (int64_t i = 0; i < N; ++i) perm[i] = i;
+        return 0;
+    }
+    if (s->order == ORC_ORDER_HILBERT) {
+        if (s->ndim != 2 || s->grid[0] != s->grid[1]) return -1;
+        return orc_hilbert(s->grid[0], perm);
+    }
+    if (s->order == ORC_ORDER_TILED) {
+        const int64_t g0 = extent(s, 0), g1 = extent(s, 1), g2 = extent(s, 2);
+        const int64_t t0 = s->ndim > 0 ? s->tile[0] : 1;
+        const int64_t t1 = s->ndim > 1 ? s->tile[1] : 1;
+        const int64_t t2 = s->ndim > 2 ? s->tile[2] : 1;
+        if (t0 < 1 || t1 < 1 || t2 < 1) return -1;
+        int64_t k = 0;
+        for (int64_t a = 0; a < g0; a += t0)
+            for (int64_t b = 0; b < g1; b += t1)
+                for (int64_t c = 0; c < g2; c += t2)
+                    for (int64_t x = a; x < imin(a + t0, g0); ++x)
+                        for (int64_t y = b; y < imin(b + t1, g1); ++y)
+                            for (int64_t z = c; z < imin(c + t2, g2); ++z)
+                                perm[k++] = (x * g1 + y) * g2 + z;
+        return 0;
+    }
+    return -1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Neighbourhoods of tokens.                                                */
+/* ------------------------------------------------------------------------ */
+
+static int cmp_i64(const void* a, const void* b) {
+    const int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+    return (x > y) - (x < y);
+}
+
+int64_t orc_neighbors(const orc_spec* s, const int64_t* perm, const int64_t* pos_of_token,
+                      int64_t i, int64_t* out) {
+    const int64_t N = orc_num_tokens(s);
+    if (s->order == ORC_ORDER_HILBERT) {
+        /* The rule acts on positions along the curve; keys are mapped back to
+           row-major tokens. */
+        const int64_t p = pos_of_token[i];
+        const int64_t n = orc_rule_set(&s->rule[0], N, p, out);
+        for (int64_t t = 0; t < n; ++t) out[t] = perm[out[t]];
+        qsort(out, (size_t)n, sizeof(int64_t), cmp_i64);
+        return n;
+    }
+    /* N-D: the set is the Cartesian product of the per-dimension sets. */
+    const int64_t g0 = extent(s, 0), g1 = extent(s, 1), g2 = extent(s, 2);
+    const int64_t c0 = i / (g1 * g2), c1 = (i / g2) % g1, c2 = i % g2;
+    int64_t* s0 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(g0 + g1 + g2));
+    int64_t* s1 = s0 + g0;
+    int64_t* s2 = s1 + g1;
+    const orc_rule whole = {ORC_WINDOW, 1, 1, 0, 1, 1, 1, 1};
+    const int64_t n0 = orc_rule_set(&s->rule[0], g0, c0, s0);
+    const int64_t n1 = orc_rule_set(s->ndim > 1 ? &s->rule[1] : &whole, g1, c1, s1);
+    const int64_t n2 = orc_rule_set(s->ndim > 2 ? &s->rule[2] : &whole, g2, c2, s2);
+    int64_t n = 0;
+    for (int64_t a = 0; a < n0; ++a)
+        for (int64_t b = 0; b < n1; ++b)
+            for (int64_t c = 0; c < n2; ++c) out[n++] = (s0[a] * g1 + s1[b]) * g2 + s2[c];
+    free(s0);
+    return n;
+}
+
+/* Inverse of perm. */
+static int64_t* invert(const int64_t* perm, int64_t N) {
+    int64_t* inv = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    for (int64_t p = 0; p < N; ++p) inv[perm[p]] = p;
+    return inv;
+}
+
+int64_t orc_attended_pairs(const orc_spec* s) {
+    const int64_t N = orc_num_tokens(s);
+    int64_t* perm = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (orc_order(s, perm) != 0) {
+        free(perm);
+        return -1;
+    }
+    int64_t* pos = invert(perm, N);
+    int64_t total = 0;
+#pragma omp parallel reduction(+ : total)
+    {
+        int64_t* buf = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t i = 0; i < N; ++i) total += orc_neighbors(s, perm, pos, i, buf);
+        free(buf);
+    }
+    free(pos);
+    free(perm);
+    return total;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention (Eqs. 2-4 of the pi-Attention page over the set N(i)).          */
+/* ------------------------------------------------------------------------ */
+
+static double load_elem(const void* base, int32_t dtype, int64_t idx) {
+    if (dtype == 1) return (double)((const float*)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+int orc_attention(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dtype,
+                  const void* q, const void* k, const void* v, double scale,
+                  const int64_t* rows, int64_t nrows, double* out, double* lse,
+                  int32_t threads) {
+    const int64_t N = orc_num_tokens(s);
+    int64_t* perm = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (orc_order(s, perm) != 0) {
+        free(perm);
+        return -1;
+    }
+    int64_t* pos = invert(perm, N);
+    const int64_t total = B * H * nrows;
+    int err = 0;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+        double* z = (double*)malloc(sizeof(double) * (size_t)N);
+        double* qi = (double*)malloc(sizeof(double) * (size_t)D);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < total; ++t) {
+            const int64_t bh = t / nrows, r = t % nrows;
+            const int64_t i = rows ? rows[r] : r;
+            if (i < 0 || i >= N) {
+                err = 1;
+                continue;
+            }
+            const int64_t head = bh * N * D;
+            for (int64_t d = 0; d < D; ++d) qi[d] = load_elem(q, dtype, head + i * D + d);
+            const int64_t n = orc_neighbors(s, perm, pos, i, nb);
+            double* o = out + t * D;
+            if (n == 0) {
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                lse[t] = -INFINITY;
+                continue;
+            }
+            /* z_ij = scale * q_i . k_j  (Eq. 4 with the scale passed in) */
+            double m = -INFINITY;
+            for (int64_t a = 0; a < n; ++a) {
+                const int64_t kj = head + nb[a] * D;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d) dot += qi[d] * load_elem(k, dtype, kj + d);
+                z[a] = scale * dot;
+                if (z[a] > m) m = z[a];
+            }
+            /* alpha_ij = exp(z_ij) / sum_j' exp(z_ij') (Eq. 2), written with the
+               row maximum factored out; output = sum_j alpha_ij v_j (Eq. 3). */
+            double l = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int64_t a = 0; a < n; ++a) {
+                const double e = exp(z[a] - m);
+                l += e;
+                const int64_t vj = head + nb[a] * D;
+                for (int64_t d = 0; d < D; ++d) acc[d] += e * load_elem(v, dtype, vj + d);
+            }
+            for (int64_t d = 0; d < D; ++d) o[d] = acc[d] / l;
+            lse[t] = m + log(l);
+        }
+        free(acc);
+        free(qi);
+        free(z);
+        free(nb);
+    }
+    free(pos);
+    free(perm);
+    return err ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tile classes.                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Every attended pair (i, j) is counted in the cell (tile of the position of
+   i, tile of the position of j).  A cell with no pair is empty; one whose
+   count equals (valid queries) x (valid keys) of the two tiles is full; any
+   other is partial ("Hilbert-Guided Sparse Local Attention", methodology). */
+int orc_tile_classes(const orc_spec* s, int64_t q_block, int64_t kv_block, uint8_t* cls,
+                     int64_t* pairs, int32_t threads) {
+    const int64_t N = orc_num_tokens(s);
+    if (q_block < 1 || kv_block < 1) return -1;
+    int64_t* perm = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (orc_order(s, perm) != 0) {
+        free(perm);
+        return -1;
+    }
+    int64_t* pos = invert(perm, N);
+    const int64_t nqt = ceil_div(N, q_block), nkt = ceil_div(N, kv_block);
+    int64_t* cnt = (int64_t*)calloc((size_t)(nqt * nkt), sizeof(int64_t));
+    int64_t total = 0;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel reduction(+ : total)
+    {
+        int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t qt = 0; qt < nqt; ++qt) {
+            int64_t* row = cnt + qt * nkt;
+            for (int64_t p = qt * q_block; p < imin((qt + 1) * q_block, N); ++p) {
+                const int64_t n = orc_neighbors(s, perm, pos, perm[p], nb);
+                total += n;
+                for (int64_t a = 0; a < n; ++a) row[pos[nb[a]] / kv_block] += 1;
+            }
+        }
+        free(nb);
+    }
+    for (int64_t qt = 0; qt < nqt; ++qt) {
+        const int64_t nq = imin(q_block, N - qt * q_block);
+        for (int64_t kt = 0; kt < nkt; ++kt) {
+            const int64_t nk = imin(kv_block, N - kt * kv_block);
+            const int64_t c = cnt[qt * nkt + kt];
+            cls[qt * nkt + kt] = c == 0 ? 0 : (c == nq * nk ? 2 : 1);
+        }
+    }
+    *pairs = total;
+    free(cnt);
+    free(pos);
+    free(perm);
+    return 0;
+}
