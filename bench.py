@@ -1,0 +1,180 @@
+"""Benchmark: one step = one forward of the N-D local-attention hot path over one
+batch of synthetic input, by default the 3-D sliding-tile workload (batch 1,
+24 heads, head_dim 128, 30x48x80 tokens, 6x8x8 tiles, 3x5x7-tile window).
+
+Prints ONE JSON line: effective TFLOP/s (only unmasked QK^T + PV flops,
+4 * D * attended pairs * B * H per step), the roofline of the attention kernel
+(MFMA bound, MI355X dense bf16 peak), and the fp64 CPU oracle timed on a
+bounded sample of the same workload as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, 3D sliding-tile attn"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA (published)
+PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_fwd_sta3d_pmc.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def read_traffic(kernel_sig: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current kernel source (null otherwise)."""
+    try:
+        with open(PROFILE_PMC) as f:
+            for line in f:
+                if line.startswith("traffic_json:"):
+                    d = json.loads(line.split(":", 1)[1])
+                    if d.get("kernel_sig") == kernel_sig:
+                        return d.get("bytes_per_launch")
+    except OSError:
+        pass
+    return None
+
+
+def kernel_signature() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "dimensional_sparse_local_amd", "csrc", "attn_fwd.hip")
+    with open(src, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, q, k, v, scale, target_s: float):
+    """The oracle as it stands, on all host cores, over a bounded sample of
+    query rows of one (batch, head) of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    q1, k1, v1 = (x[:1, :1].cpu().contiguous() for x in (q, k, v))
+    n = q1.shape[2]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(n)
+    threads = oracle.max_threads()
+
+    def run(count):
+        rows = np.sort(order[:count]).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention(wl, q1, k1, v1, scale, rows=rows)
+        dt = time.perf_counter() - t0
+        pairs = sum(len(oracle.neighbors(wl, int(r))) for r in rows[: min(len(rows), 64)])
+        pairs = pairs * len(rows) / min(len(rows), 64)
+        return dt, pairs, len(rows)
+
+    dt, _, c = run(min(n, 4 * threads))
+    per_row = dt / c
+    count = int(min(n, max(c, target_s / max(per_row, 1e-9))))
+    dt, pairs, c = run(count)
+    flops = 4.0 * int(wl["D"]) * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d query rows of batch 0, head 0 (%.3g effective flops) in %.1f s, fp64, "
+                      "OpenMP" % (c, flops, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--q-block", type=int, default=0)
+    ap.add_argument("--permute-passes", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the (batch, head) slices shard with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dimensional_sparse_local_amd import na
+    from dimensional_sparse_local_amd import workloads as W
+
+    name = args.workload or W.HEADLINE
+    wl = W.CONFIGS[name]
+    B, H, D = int(wl["B"]), int(wl["H"]), int(wl["D"])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    plan = na.Plan(wl, q_block=args.q_block)
+    flops = plan.effective_flops(B, H)
+    q, k, v = W.make_qkv(wl, device=dev)
+    scale = W.default_scale(wl)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, plan.n_tokens), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    log("bench: %s plan %s" % (name, plan.stats))
+
+    def step():
+        plan.forward(q, k, v, out=out, lse=lse, scale=scale, permute_passes=args.permute_passes)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log("bench: %.3f ms/step" % ms)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl["dtype"]]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
+        cpu = cpu_baseline(wl, q, k, v, scale, args.cpu_seconds)
+
+    sig = kernel_signature()
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl["dtype"],
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "heads": H, "head_dim": D, "grid": wl["grid"],
+                   "order": wl["order"], "pattern": wl["pattern"],
+                   "q_block": plan.stats["q_block"], "kv_block": plan.stats["kv_block"],
+                   "attended_pairs_per_head": plan.stats["attended_pairs"],
+                   "effective_flops_per_step": flops,
+                   "pct_of_peak": round(100.0 * tflops / peak, 2),
+                   "permute_passes": bool(args.permute_passes)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": read_traffic(sig), "kernel_sig": sig},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

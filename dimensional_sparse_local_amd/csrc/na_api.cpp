@@ -1,0 +1,388 @@
+// C ABI of libna.so: plan lifetime, validation, device upload and kernel
+// dispatch.  Every entry point returns an na_status and never throws; all
+// argument checks run on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "na_internal.h"
+
+namespace {
+thread_local char g_err[512] = "";
+
+const char* hip_err(hipError_t e) { return hipGetErrorString(e); }
+
+template <typename T>
+na_status upload(const std::vector<T>& host, T** dev) {
+    *dev = nullptr;
+    if (host.empty()) return NA_OK;
+    const size_t bytes = host.size() * sizeof(T);
+    hipError_t e = hipMalloc((void**)dev, bytes);
+    if (e != hipSuccess) {
+        *dev = nullptr;
+        na_set_error("hipMalloc(%zu) failed: %s", bytes, hip_err(e));
+        return e == hipErrorOutOfMemory ? NA_ERR_OUT_OF_MEMORY : NA_ERR_DEVICE;
+    }
+    e = hipMemcpy(*dev, host.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        na_set_error("hipMemcpy(%zu) failed: %s", bytes, hip_err(e));
+        return NA_ERR_DEVICE;
+    }
+    return NA_OK;
+}
+
+void free_device(na_plan_s* p) {
+    if (!p->on_device) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != p->device) (void)hipSetDevice(p->device);
+    (void)hipFree(p->d_perm);
+    (void)hipFree(p->d_row_ptr);
+    (void)hipFree(p->d_entries);
+    (void)hipFree(p->d_kcoord);
+    (void)hipFree(p->d_qbox);
+    if (cur != p->device && cur >= 0) (void)hipSetDevice(cur);
+    p->d_perm = nullptr;
+    p->d_row_ptr = nullptr;
+    p->d_entries = nullptr;
+    p->d_kcoord = nullptr;
+    p->d_qbox = nullptr;
+    p->on_device = false;
+}
+
+int elem_bytes(const na_plan_s* p) { return p->desc.dtype == NA_F32 ? 4 : 2; }
+
+// Validate one [B, H, N, D] tensor view against the plan.
+na_status check_tensor(const na_plan_s* p, const na_tensor* t, const char* name, int64_t B,
+                       int64_t H) {
+    if (!t || !t->ptr) {
+        na_set_error("%s is NULL", name);
+        return NA_ERR_INVALID_ARG;
+    }
+    const int64_t D = p->desc.head_dim;
+    const int64_t align = 16 / elem_bytes(p);  // elements per 16 bytes
+    if (((uintptr_t)t->ptr) % 16 != 0) {
+        na_set_error("%s must be 16-byte aligned", name);
+        return NA_ERR_INVALID_ARG;
+    }
+    if (t->stride_n < D || t->stride_n % align != 0 || t->stride_h % align != 0 ||
+        t->stride_b % align != 0 || t->stride_h < 0 || t->stride_b < 0) {
+        na_set_error("%s strides (b=%lld h=%lld n=%lld) must be non-negative multiples of %lld "
+                     "with stride_n >= head_dim",
+                     name, (long long)t->stride_b, (long long)t->stride_h, (long long)t->stride_n,
+                     (long long)align);
+        return NA_ERR_INVALID_ARG;
+    }
+    (void)B;
+    (void)H;
+    return NA_OK;
+}
+
+}  // namespace
+
+void na_set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+}
+
+extern "C" {
+
+const char* na_last_error(void) { return g_err; }
+
+int32_t na_abi_version(void) { return NA_ABI_VERSION; }
+
+const char* na_status_string(na_status s) {
+    switch (s) {
+        case NA_OK: return "ok";
+        case NA_ERR_INVALID_ARG: return "invalid argument";
+        case NA_ERR_UNSUPPORTED: return "unsupported";
+        case NA_ERR_OUT_OF_MEMORY: return "out of memory";
+        case NA_ERR_DEVICE: return "device error";
+        case NA_ERR_PLAN_MISMATCH: return "plan mismatch";
+    }
+    return "unknown status";
+}
+
+na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* out) {
+    if (!out) {
+        na_set_error("plan output pointer is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    *out = nullptr;
+    if (flags & ~NA_PLAN_HOST_ONLY) {
+        na_set_error("unknown plan flags 0x%x", flags);
+        return NA_ERR_INVALID_ARG;
+    }
+    na_plan_s* p = new (std::nothrow) na_plan_s();
+    if (!p) {
+        na_set_error("host allocation failed");
+        return NA_ERR_OUT_OF_MEMORY;
+    }
+    na_status st;
+    try {
+        st = na_plan_build_host(desc, p);
+    } catch (const std::bad_alloc&) {
+        na_set_error("host allocation failed while planning");
+        st = NA_ERR_OUT_OF_MEMORY;
+    }
+    if (st != NA_OK) {
+        delete p;
+        return st;
+    }
+    if (!(flags & NA_PLAN_HOST_ONLY)) {
+        hipError_t e = hipGetDevice(&p->device);
+        if (e != hipSuccess) {
+            na_set_error("hipGetDevice failed: %s", hip_err(e));
+            delete p;
+            return NA_ERR_DEVICE;
+        }
+        p->on_device = true;
+        const std::vector<int32_t> none;
+        st = upload(p->identity_order ? none : p->perm, &p->d_perm);
+        if (st == NA_OK) st = upload(p->row_ptr, &p->d_row_ptr);
+        if (st == NA_OK) st = upload(p->entries, &p->d_entries);
+        if (st == NA_OK && p->has_partial) st = upload(p->kcoord, &p->d_kcoord);
+        if (st == NA_OK && p->has_partial) st = upload(p->qbox, &p->d_qbox);
+        if (st == NA_OK && !p->identity_order && !p->d_perm) st = NA_ERR_DEVICE;
+        if (st != NA_OK) {
+            free_device(p);
+            delete p;
+            return st;
+        }
+    }
+    *out = p;
+    return NA_OK;
+}
+
+na_status na_plan_destroy(na_plan_t p) {
+    if (!p) return NA_OK;
+    free_device(p);
+    delete p;
+    return NA_OK;
+}
+
+na_status na_plan_get_stats(na_plan_t p, na_plan_stats* s) {
+    if (!p || !s) {
+        na_set_error("plan or stats pointer is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    *s = p->stats;
+    return NA_OK;
+}
+
+na_status na_plan_get_classes(na_plan_t p, uint8_t* host, size_t n) {
+    if (!p || !host) {
+        na_set_error("plan or output pointer is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    const int64_t nq = p->stats.n_q_tiles, nk = p->stats.n_kv_tiles;
+    if ((int64_t)n < nq * nk) {
+        na_set_error("class buffer holds %zu entries, need %lld", n, (long long)(nq * nk));
+        return NA_ERR_INVALID_ARG;
+    }
+    std::memset(host, 0, (size_t)(nq * nk));
+    for (int64_t qt = 0; qt < nq; ++qt)
+        for (int32_t e = p->row_ptr[qt]; e < p->row_ptr[qt + 1]; ++e) {
+            const uint32_t ent = p->entries[e];
+            host[qt * nk + (ent & ~NA_ENTRY_PARTIAL)] = (ent & NA_ENTRY_PARTIAL) ? 1 : 2;
+        }
+    return NA_OK;
+}
+
+na_status na_plan_get_order(na_plan_t p, int32_t* host, size_t n) {
+    if (!p || !host) {
+        na_set_error("plan or output pointer is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    if ((int64_t)n < p->n_tokens) {
+        na_set_error("order buffer holds %zu entries, need %lld", n, (long long)p->n_tokens);
+        return NA_ERR_INVALID_ARG;
+    }
+    std::memcpy(host, p->perm.data(), sizeof(int32_t) * (size_t)p->n_tokens);
+    return NA_OK;
+}
+
+size_t na_forward_workspace_bytes(na_plan_t p, int64_t B, int64_t H, uint32_t flags) {
+    if (!p || B < 1 || H < 1) return 0;
+    if (!(flags & NA_FWD_PERMUTE_PASSES) || p->identity_order) return 0;
+    const size_t rows = (size_t)B * (size_t)H * (size_t)p->n_tokens;
+    const size_t t = rows * (size_t)p->desc.head_dim * (size_t)elem_bytes(p);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return 4 * up(t) + up(rows * sizeof(float));
+}
+
+na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, const na_tensor* k,
+                     const na_tensor* v, const na_tensor* out, float* lse, float scale,
+                     uint32_t flags, void* workspace, size_t ws_bytes, void* stream) {
+    if (!p) {
+        na_set_error("plan is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (!p->on_device) {
+        na_set_error("plan was built host-only and cannot run");
+        return NA_ERR_PLAN_MISMATCH;
+    }
+    if (flags & ~NA_FWD_PERMUTE_PASSES) {
+        na_set_error("unknown forward flags 0x%x", flags);
+        return NA_ERR_INVALID_ARG;
+    }
+    if (B < 1 || H < 1) {
+        na_set_error("B and H must be >= 1");
+        return NA_ERR_INVALID_ARG;
+    }
+    const int64_t n_wg = p->stats.n_q_tiles * B * H;
+    if (n_wg > 0x7fffffff || B * H > 0x7fffffff / (p->n_tokens > 0 ? p->n_tokens : 1)) {
+        na_set_error("B * H * tiles too large");
+        return NA_ERR_INVALID_ARG;
+    }
+    na_status st;
+    if ((st = check_tensor(p, q, "q", B, H)) != NA_OK) return st;
+    if ((st = check_tensor(p, k, "k", B, H)) != NA_OK) return st;
+    if ((st = check_tensor(p, v, "v", B, H)) != NA_OK) return st;
+    if ((st = check_tensor(p, out, "out", B, H)) != NA_OK) return st;
+    if (lse && ((uintptr_t)lse) % 4 != 0) {
+        na_set_error("lse must be 4-byte aligned");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) {
+        na_set_error("scale must be finite");
+        return NA_ERR_INVALID_ARG;
+    }
+    const na_plan_desc& d = p->desc;
+    if (!na_attn_supported(d.dtype, d.head_dim, d.q_block, d.kv_block)) {
+        na_set_error("no kernel for dtype=%d head_dim=%d q_block=%d kv_block=%d", d.dtype,
+                     d.head_dim, d.q_block, d.kv_block);
+        return NA_ERR_UNSUPPORTED;
+    }
+    int cur = -1;
+    hipError_t he = hipGetDevice(&cur);
+    if (he != hipSuccess || cur != p->device) {
+        na_set_error("plan lives on device %d, current device is %d", p->device, cur);
+        return NA_ERR_PLAN_MISMATCH;
+    }
+    const bool passes = (flags & NA_FWD_PERMUTE_PASSES) && !p->identity_order;
+    if (passes) {
+        const size_t need = na_forward_workspace_bytes(p, B, H, flags);
+        if (!workspace || ws_bytes < need || ((uintptr_t)workspace) % 256 != 0) {
+            na_set_error("permute passes need %zu bytes of 256-byte aligned workspace", need);
+            return NA_ERR_INVALID_ARG;
+        }
+    }
+
+    NaAttnParams a{};
+    a.n_tokens = (int32_t)p->n_tokens;
+    a.heads = (int32_t)H;
+    a.n_q_tiles = (int32_t)p->stats.n_q_tiles;
+    a.n_wg = (int32_t)n_wg;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.row_ptr = p->d_row_ptr;
+    a.entries = p->d_entries;
+    a.kcoord = p->d_kcoord;
+    a.qbox = p->d_qbox;
+    a.pdims = p->pdims;
+    a.has_dilation = p->has_dilation ? 1 : 0;
+    a.dil0 = d.dilation[0];
+    a.dil1 = d.dilation[1];
+    a.dil2 = d.dilation[2];
+    a.lse = lse;
+    const int64_t N = p->n_tokens, D = d.head_dim, eb = elem_bytes(p);
+
+    if (n_wg == 0) return NA_OK;
+    int rc = 0;
+    if (!passes) {
+        a.q = q->ptr;
+        a.k = k->ptr;
+        a.v = v->ptr;
+        a.out = out->ptr;
+        a.q_sb = q->stride_b, a.q_sh = q->stride_h, a.q_sn = q->stride_n;
+        a.k_sb = k->stride_b, a.k_sh = k->stride_h, a.k_sn = k->stride_n;
+        a.v_sb = v->stride_b, a.v_sh = v->stride_h, a.v_sn = v->stride_n;
+        a.o_sb = out->stride_b, a.o_sh = out->stride_h, a.o_sn = out->stride_n;
+        a.perm = p->identity_order ? nullptr : p->d_perm;
+        rc = na_attn_launch(a, d.dtype, d.head_dim, d.q_block, stream);
+    } else {
+        // gather q, k, v into sequence order, attend on contiguous tiles, scatter back
+        auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+        const size_t t = (size_t)(B * H * N * D * eb);
+        char* ws = (char*)workspace;
+        void* qs = ws;
+        void* ks = ws + up(t);
+        void* vs = ws + 2 * up(t);
+        void* os = ws + 3 * up(t);
+        float* ls = (float*)(ws + 4 * up(t));
+        const int64_t csb = H * N * D * eb, csh = N * D * eb, csn = D * eb;
+        const na_tensor* src[3] = {q, k, v};
+        void* dst[3] = {qs, ks, vs};
+        for (int i = 0; i < 3 && rc == 0; ++i)
+            rc = na_permute_launch(src[i]->ptr, dst[i], B, H, N, D * eb, src[i]->stride_b * eb,
+                                   src[i]->stride_h * eb, src[i]->stride_n * eb, csb, csh, csn,
+                                   p->d_perm, 0, stream);
+        if (rc == 0) {
+            a.q = qs, a.k = ks, a.v = vs, a.out = os;
+            a.q_sb = a.k_sb = a.v_sb = a.o_sb = H * N * D;
+            a.q_sh = a.k_sh = a.v_sh = a.o_sh = N * D;
+            a.q_sn = a.k_sn = a.v_sn = a.o_sn = D;
+            a.perm = nullptr;
+            a.lse = lse ? ls : nullptr;
+            rc = na_attn_launch(a, d.dtype, d.head_dim, d.q_block, stream);
+        }
+        if (rc == 0)
+            rc = na_permute_launch(os, out->ptr, B, H, N, D * eb, csb, csh, csn,
+                                   out->stride_b * eb, out->stride_h * eb, out->stride_n * eb,
+                                   p->d_perm, 1, stream);
+        if (rc == 0 && lse)
+            rc = na_permute_launch(ls, lse, B, H, N, 4, H * N * 4, N * 4, 4, H * N * 4, N * 4, 4,
+                                   p->d_perm, 1, stream);
+    }
+    if (rc != 0) {
+        na_set_error("kernel launch failed: %s", hip_err((hipError_t)rc));
+        return NA_ERR_DEVICE;
+    }
+    return NA_OK;
+}
+
+na_status na_permute(na_plan_t p, int64_t B, int64_t H, const na_tensor* in, const na_tensor* out,
+                     int32_t inverse, void* stream) {
+    if (!p) {
+        na_set_error("plan is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (!p->on_device) {
+        na_set_error("plan was built host-only and cannot run");
+        return NA_ERR_PLAN_MISMATCH;
+    }
+    if (B < 1 || H < 1 || (inverse != 0 && inverse != 1)) {
+        na_set_error("B, H must be >= 1 and inverse 0 or 1");
+        return NA_ERR_INVALID_ARG;
+    }
+    na_status st;
+    if ((st = check_tensor(p, in, "in", B, H)) != NA_OK) return st;
+    if ((st = check_tensor(p, out, "out", B, H)) != NA_OK) return st;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != p->device) {
+        na_set_error("plan lives on device %d, current device is %d", p->device, cur);
+        return NA_ERR_PLAN_MISMATCH;
+    }
+    if (p->identity_order) {
+        na_set_error("the plan's order is the identity: nothing to permute");
+        return NA_ERR_UNSUPPORTED;
+    }
+    const int64_t eb = elem_bytes(p);
+    int rc;
+    rc = na_permute_launch(in->ptr, out->ptr, B, H, p->n_tokens, p->desc.head_dim * eb,
+                           in->stride_b * eb, in->stride_h * eb, in->stride_n * eb,
+                           out->stride_b * eb, out->stride_h * eb, out->stride_n * eb, p->d_perm,
+                           inverse, stream);
+    if (rc != 0) {
+        na_set_error("permute launch failed: %s", hip_err((hipError_t)rc));
+        return NA_ERR_DEVICE;
+    }
+    return NA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,360 @@
+// Host planner: token order, per-position window boxes, and the exact
+// classification of every (query tile, key/value tile) pair into empty,
+// partial or full ("Hilbert-Guided Sparse Local Attention", "Methodology in
+// Plain English": empty tiles are skipped, partial tiles need element-wise
+// masks).  Built once per shape; the result is immutable.
+//
+// Window rule per pattern dimension (see include/na.h): sliding window of
+// `window` positions starting at the (stride-group) centre minus `left`,
+// shifted inside the axis (neighbourhood attention, "Generalized Neighborhood
+// Attention", abstract) or cut at its ends (band / slide attention,
+// "pi-Attention", Eq. 5), on the dilation sub-grid of the query.
+#include <algorithm>
+#include <cstring>
+#include <limits>
+
+#include "na_internal.h"
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+
+// Hilbert curve index -> cell, by the standard bit-by-bit construction: at each
+// scale s the two bits of the index pick a quadrant, and the coordinates built
+// so far are reflected / transposed into that quadrant's frame.  With row = y
+// and col = x the curve starts at (0, 0) and ends at (0, n - 1).
+void hilbert_cell(int64_t n, int64_t d, int64_t* row, int64_t* col) {
+    int64_t x = 0, y = 0, t = d;
+    for (int64_t s = 1; s < n; s *= 2) {
+        const int64_t rx = 1 & (t / 2);
+        const int64_t ry = 1 & (t ^ rx);
+        if (ry == 0) {
+            if (rx == 1) {
+                x = s - 1 - x;
+                y = s - 1 - y;
+            }
+            std::swap(x, y);
+        }
+        x += s * rx;
+        y += s * ry;
+        t /= 4;
+    }
+    *row = y;
+    *col = x;
+}
+
+struct Axis {
+    int64_t L, w, left, stride, dil;
+    bool clamp;
+};
+
+// [lo, hi) of the keys of coordinate x on one axis, in axis coordinates; with
+// dilation only positions congruent to lo modulo dil inside it count.
+void axis_window(const Axis& a, int64_t x, int32_t* lo, int32_t* hi) {
+    const int64_t g = x % a.dil;
+    const int64_t xl = x / a.dil;
+    const int64_t Lg = ceil_div(a.L - g, a.dil);
+    const int64_t c = (xl / a.stride) * a.stride + a.stride / 2;
+    int64_t s, e;
+    if (a.clamp) {
+        if (a.w >= Lg) {
+            s = 0;
+            e = Lg;
+        } else {
+            s = std::min(std::max(c - a.left, int64_t(0)), Lg - a.w);
+            e = s + a.w;
+        }
+    } else {
+        s = std::max(c - a.left, int64_t(0));
+        e = std::min(c - a.left + a.w, Lg);
+    }
+    if (e <= s) {
+        *lo = 0;
+        *hi = 0;
+        return;
+    }
+    *lo = (int32_t)(g + a.dil * s);
+    *hi = (int32_t)(g + a.dil * (e - 1) + 1);
+}
+
+bool inside(const int32_t* box, const int32_t* c, int pdims, const int32_t* dil) {
+    for (int d = 0; d < pdims; ++d) {
+        if (c[d] < box[d] || c[d] >= box[3 + d]) return false;
+        if (dil[d] > 1 && (c[d] - box[d]) % dil[d] != 0) return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
+    if (!in) {
+        na_set_error("descriptor is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    na_plan_desc d = *in;
+    if (d.ndim < 1 || d.ndim > 3) {
+        na_set_error("ndim must be 1, 2 or 3 (got %d)", d.ndim);
+        return NA_ERR_INVALID_ARG;
+    }
+    int64_t N = 1;
+    for (int i = 0; i < d.ndim; ++i) {
+        if (d.grid[i] < 1) {
+            na_set_error("grid[%d] must be >= 1", i);
+            return NA_ERR_INVALID_ARG;
+        }
+        N *= d.grid[i];
+    }
+    for (int i = d.ndim; i < 3; ++i) d.grid[i] = 1;
+    if (N > std::numeric_limits<int32_t>::max() / 2) {
+        na_set_error("too many tokens (%lld)", (long long)N);
+        return NA_ERR_INVALID_ARG;
+    }
+    if (d.order < NA_ORDER_ROW_MAJOR || d.order > NA_ORDER_HILBERT) {
+        na_set_error("unknown order %d", d.order);
+        return NA_ERR_INVALID_ARG;
+    }
+    if (d.dtype != NA_BF16 && d.dtype != NA_F32) {
+        na_set_error("unknown dtype %d", d.dtype);
+        return NA_ERR_INVALID_ARG;
+    }
+    if (d.head_dim < 1) {
+        na_set_error("head_dim must be >= 1");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (d.q_block == 0) d.q_block = d.dtype == NA_F32 ? NA_Q_BLOCK_F32 : 128;
+    if (d.kv_block == 0) d.kv_block = d.dtype == NA_F32 ? NA_KV_BLOCK_F32 : NA_KV_BLOCK_BF16;
+    if (d.q_block < 1 || d.kv_block < 1) {
+        na_set_error("q_block and kv_block must be >= 1");
+        return NA_ERR_INVALID_ARG;
+    }
+    const int pdims = d.order == NA_ORDER_HILBERT ? 1 : d.ndim;
+    if (d.order == NA_ORDER_HILBERT) {
+        if (d.ndim != 2 || d.grid[0] != d.grid[1] || !is_pow2(d.grid[0])) {
+            na_set_error("Hilbert order needs a square power-of-two 2-D grid");
+            return NA_ERR_UNSUPPORTED;
+        }
+    }
+    if (d.order == NA_ORDER_TILED) {
+        for (int i = 0; i < d.ndim; ++i)
+            if (d.tile[i] < 1) {
+                na_set_error("tile[%d] must be >= 1", i);
+                return NA_ERR_INVALID_ARG;
+            }
+        for (int i = d.ndim; i < 3; ++i) d.tile[i] = 1;
+    }
+    Axis ax[3];
+    for (int i = 0; i < 3; ++i) {
+        if (i >= pdims) {
+            ax[i] = Axis{1, 1, 0, 1, 1, true};
+            p->plen[i] = 1;
+            p->left[i] = 0;
+            p->clamp[i] = 1;
+            d.window[i] = 1;
+            d.window_left[i] = 0;
+            d.stride[i] = 1;
+            d.dilation[i] = 1;
+            d.causal[i] = 0;
+            d.boundary[i] = NA_BOUND_CLAMP;
+            continue;
+        }
+        const int64_t L = d.order == NA_ORDER_HILBERT ? N : d.grid[i];
+        if (d.window[i] < 1 || d.stride[i] < 1 || d.dilation[i] < 1) {
+            na_set_error("window, stride and dilation of dimension %d must be >= 1", i);
+            return NA_ERR_INVALID_ARG;
+        }
+        if (d.stride[i] > d.window[i]) {
+            // a group wider than its window would not see all of itself
+            na_set_error("stride[%d] (%d) must not exceed window[%d] (%d)", i, d.stride[i], i,
+                         d.window[i]);
+            return NA_ERR_INVALID_ARG;
+        }
+        if (d.causal[i] != 0 && d.causal[i] != 1) {
+            na_set_error("causal[%d] must be 0 or 1", i);
+            return NA_ERR_INVALID_ARG;
+        }
+        if (d.boundary[i] != NA_BOUND_CLAMP && d.boundary[i] != NA_BOUND_TRUNCATE) {
+            na_set_error("boundary[%d] must be NA_BOUND_CLAMP or NA_BOUND_TRUNCATE", i);
+            return NA_ERR_INVALID_ARG;
+        }
+        int64_t left = d.window_left[i];
+        if (d.causal[i]) {
+            left = d.window[i] - 1;
+            d.boundary[i] = NA_BOUND_TRUNCATE;
+        } else if (left < 0) {
+            if (left != -1) {
+                na_set_error("window_left[%d] must be >= 0 or -1", i);
+                return NA_ERR_INVALID_ARG;
+            }
+            left = d.window[i] / 2;
+        }
+        d.window_left[i] = (int32_t)left;
+        ax[i] = Axis{L, d.window[i], left, d.stride[i], d.dilation[i],
+                     d.boundary[i] == NA_BOUND_CLAMP};
+        p->plen[i] = (int32_t)L;
+        p->left[i] = (int32_t)left;
+        p->clamp[i] = d.boundary[i] == NA_BOUND_CLAMP;
+        if (d.dilation[i] > 1) p->has_dilation = true;
+    }
+    p->desc = d;
+    p->n_tokens = N;
+    p->pdims = pdims;
+
+    // ---- token order ----------------------------------------------------
+    p->perm.resize(N);
+    if (d.order == NA_ORDER_ROW_MAJOR) {
+        for (int64_t i = 0; i < N; ++i) p->perm[i] = (int32_t)i;
+        p->identity_order = true;
+    } else if (d.order == NA_ORDER_HILBERT) {
+        const int64_t n = d.grid[0];
+        for (int64_t t = 0; t < N; ++t) {
+            int64_t r, c;
+            hilbert_cell(n, t, &r, &c);
+            p->perm[t] = (int32_t)(r * n + c);
+        }
+        p->identity_order = false;
+    } else {
+        const int64_t g1 = d.grid[1], g2 = d.grid[2];
+        const int64_t nt0 = ceil_div(d.grid[0], d.tile[0]);
+        const int64_t nt1 = ceil_div(g1, d.tile[1]);
+        const int64_t nt2 = ceil_div(g2, d.tile[2]);
+        int64_t pos = 0;
+        for (int64_t a = 0; a < nt0; ++a)
+            for (int64_t b = 0; b < nt1; ++b)
+                for (int64_t c = 0; c < nt2; ++c) {
+                    const int64_t x0 = a * d.tile[0], x1 = std::min<int64_t>(x0 + d.tile[0], d.grid[0]);
+                    const int64_t y0 = b * d.tile[1], y1 = std::min<int64_t>(y0 + d.tile[1], g1);
+                    const int64_t z0 = c * d.tile[2], z1 = std::min<int64_t>(z0 + d.tile[2], g2);
+                    for (int64_t x = x0; x < x1; ++x)
+                        for (int64_t y = y0; y < y1; ++y)
+                            for (int64_t z = z0; z < z1; ++z)
+                                p->perm[pos++] = (int32_t)((x * g1 + y) * g2 + z);
+                }
+        p->identity_order = true;
+        for (int64_t i = 0; i < N; ++i)
+            if (p->perm[i] != i) {
+                p->identity_order = false;
+                break;
+            }
+    }
+
+    // ---- pattern coordinates and window boxes per sequence position ------
+    p->kcoord.assign(N * 4, 0);
+    p->qbox.assign(N * 8, 0);
+    int64_t pairs = 0;
+    for (int64_t pos = 0; pos < N; ++pos) {
+        int32_t* c = &p->kcoord[pos * 4];
+        if (d.order == NA_ORDER_HILBERT) {
+            c[0] = (int32_t)pos;
+        } else {
+            const int64_t tok = p->perm[pos];
+            c[0] = (int32_t)(tok / ((int64_t)d.grid[1] * d.grid[2]));
+            c[1] = (int32_t)((tok / d.grid[2]) % d.grid[1]);
+            c[2] = (int32_t)(tok % d.grid[2]);
+        }
+        int32_t* box = &p->qbox[pos * 8];
+        int64_t cnt = 1;
+        for (int i = 0; i < 3; ++i) {
+            axis_window(ax[i], c[i], &box[i], &box[3 + i]);
+            const int64_t span = box[3 + i] - box[i];
+            cnt *= span <= 0 ? 0 : ceil_div(span, ax[i].dil);
+        }
+        pairs += cnt;
+    }
+
+    // ---- tile classification ---------------------------------------------
+    const int64_t qb = d.q_block, kb = d.kv_block;
+    const int64_t nqt = ceil_div(N, qb), nkt = ceil_div(N, kb);
+    int32_t dil[3] = {(int32_t)ax[0].dil, (int32_t)ax[1].dil, (int32_t)ax[2].dil};
+    // key bounding boxes of the key/value tiles
+    std::vector<int32_t> kbox(nkt * 6);
+    for (int64_t t = 0; t < nkt; ++t) {
+        int32_t* b = &kbox[t * 6];
+        for (int i = 0; i < 3; ++i) {
+            b[i] = std::numeric_limits<int32_t>::max();
+            b[3 + i] = std::numeric_limits<int32_t>::min();
+        }
+        for (int64_t pos = t * kb; pos < std::min(N, (t + 1) * kb); ++pos)
+            for (int i = 0; i < 3; ++i) {
+                b[i] = std::min(b[i], p->kcoord[pos * 4 + i]);
+                b[3 + i] = std::max(b[3 + i], p->kcoord[pos * 4 + i] + 1);
+            }
+    }
+    p->row_ptr.assign(nqt + 1, 0);
+    p->entries.clear();
+    int64_t n_partial = 0, n_full = 0;
+    for (int64_t qt = 0; qt < nqt; ++qt) {
+        const int64_t q0 = qt * qb, q1 = std::min(N, q0 + qb);
+        // intersection and union of the query boxes of this tile
+        int32_t ilo[3], ihi[3], ulo[3], uhi[3];
+        for (int i = 0; i < 3; ++i) {
+            ilo[i] = std::numeric_limits<int32_t>::min();
+            ihi[i] = std::numeric_limits<int32_t>::max();
+            ulo[i] = std::numeric_limits<int32_t>::max();
+            uhi[i] = std::numeric_limits<int32_t>::min();
+        }
+        bool any_empty_query = false;
+        for (int64_t pos = q0; pos < q1; ++pos) {
+            const int32_t* box = &p->qbox[pos * 8];
+            bool empty = false;
+            for (int i = 0; i < 3; ++i) empty |= box[3 + i] <= box[i];
+            if (empty) {
+                any_empty_query = true;
+                continue;
+            }
+            for (int i = 0; i < 3; ++i) {
+                ilo[i] = std::max(ilo[i], box[i]);
+                ihi[i] = std::min(ihi[i], box[3 + i]);
+                ulo[i] = std::min(ulo[i], box[i]);
+                uhi[i] = std::max(uhi[i], box[3 + i]);
+            }
+        }
+        for (int64_t kt = 0; kt < nkt; ++kt) {
+            const int32_t* kbx = &kbox[kt * 6];
+            bool disjoint = false;
+            for (int i = 0; i < p->pdims; ++i)
+                disjoint |= kbx[3 + i] <= ulo[i] || kbx[i] >= uhi[i];
+            if (disjoint) continue;  // empty (also when every query is empty)
+            bool full = !any_empty_query && !p->has_dilation;
+            for (int i = 0; full && i < p->pdims; ++i)
+                full = ilo[i] <= kbx[i] && kbx[3 + i] <= ihi[i];
+            int cls = 2;
+            if (!full) {
+                // exact: look for both an attended and an unattended pair
+                bool hit = false, miss = false;
+                const int64_t k0 = kt * kb, k1 = std::min(N, k0 + kb);
+                for (int64_t qp = q0; qp < q1 && !(hit && miss); ++qp)
+                    for (int64_t kp = k0; kp < k1; ++kp) {
+                        if (inside(&p->qbox[qp * 8], &p->kcoord[kp * 4], p->pdims, dil))
+                            hit = true;
+                        else
+                            miss = true;
+                        if (hit && miss) break;
+                    }
+                if (!hit) continue;
+                cls = miss ? 1 : 2;
+            }
+            if (cls == 1) {
+                ++n_partial;
+                p->entries.push_back((uint32_t)kt | NA_ENTRY_PARTIAL);
+            } else {
+                ++n_full;
+                p->entries.push_back((uint32_t)kt);
+            }
+        }
+        p->row_ptr[qt + 1] = (int32_t)p->entries.size();
+    }
+    p->has_partial = n_partial > 0;
+    p->stats.n_tokens = N;
+    p->stats.q_block = qb;
+    p->stats.kv_block = kb;
+    p->stats.n_q_tiles = nqt;
+    p->stats.n_kv_tiles = nkt;
+    p->stats.n_partial = n_partial;
+    p->stats.n_full = n_full;
+    p->stats.n_empty = nqt * nkt - n_partial - n_full;
+    p->stats.attended_pairs = pairs;
+    return NA_OK;
+}

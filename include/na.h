@@ -1,0 +1,188 @@
+/*
+ * na.h — C ABI of the MI355X (gfx950) N-dimensional local-attention library.
+ *
+ * Forward pass of softmax attention restricted to a local neighbourhood of each
+ * query on a 1-D, 2-D or 3-D token grid ("pi-Attention: Online Efficient Sparse
+ * Transformers for Long-Context Modeling", Section 3.2, Eqs. 4-5: the full sum
+ * of Eq. 3 replaced by a sum over the neighbourhood), computed as block-sparse
+ * fused attention: the token sequence is cut into query tiles and key/value
+ * tiles, every (query tile, key/value tile) pair is classified once as empty,
+ * partial or full ("Hilbert-Guided Sparse Local Attention", "Methodology in
+ * Plain English"), empty pairs are skipped and only partial pairs are masked
+ * element by element.
+ *
+ * Patterns covered (per pattern dimension: window, left offset, stride,
+ * dilation, causal flag, border rule):
+ *   - neighbourhood attention, window shifted inside at the borders, with
+ *     strided and dilated forms ("Generalized Neighborhood Attention",
+ *     abstract);
+ *   - sliding-window / band attention cut at the borders, causal or not
+ *     ("pi-Attention", Eq. 5);
+ *   - sliding tile attention: tile order plus a strided window whose stride is
+ *     the tile ("ENA: Efficient N-dimensional Attention", reading notes);
+ *   - blocked (window) attention: stride = window, cut at the borders;
+ *   - Hilbert-ordered window / slide / neighbourhood attention: tokens of a 2-D
+ *     grid reordered along a Hilbert curve, pattern formed on the 1-D curve
+ *     position ("Hilbert-Guided Sparse Local Attention", abstract).
+ *
+ * Conventions
+ *   - Tensors q, k, v, out are [B, H, N, D] with D contiguous; na_tensor carries
+ *     the base pointer and the element strides of the B, H and N axes.  Tokens
+ *     are always in row-major grid order (last grid dimension fastest), also
+ *     for Hilbert and tiled orders: reordering is internal.
+ *   - lse is float32 [B, H, N], contiguous, row-major token order: the natural
+ *     log of the sum over the neighbourhood of exp(scale * q.k).
+ *   - All device pointers are caller-owned HIP device memory on the current
+ *     device; `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *     enqueued asynchronously; nothing synchronises.
+ *   - Every call returns an na_status; nothing throws across this boundary.
+ *     Arguments are validated on the host before anything is enqueued; a
+ *     failed validation touches no device memory.  na_last_error() gives a
+ *     thread-local detail string for the last failure.
+ */
+#ifndef NA_H
+#define NA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NA_ABI_VERSION 1
+
+typedef enum {
+    NA_OK = 0,
+    NA_ERR_INVALID_ARG = 1,   /* malformed descriptor, pointer, size or stride */
+    NA_ERR_UNSUPPORTED = 2,   /* valid, but no kernel variant for it (never a silent fallback) */
+    NA_ERR_OUT_OF_MEMORY = 3, /* host or device allocation failed */
+    NA_ERR_DEVICE = 4,        /* a HIP call or kernel launch failed; see na_last_error() */
+    NA_ERR_PLAN_MISMATCH = 5  /* tensors or flags do not match the plan */
+} na_status;
+
+/* Token orders along which tiles are cut. */
+enum {
+    NA_ORDER_ROW_MAJOR = 0, /* row-major grid order */
+    NA_ORDER_TILED = 1,     /* tile by tile (tile extents in na_plan_desc.tile), row-major inside */
+    NA_ORDER_HILBERT = 2    /* 2-D square power-of-two grid along a Hilbert curve that starts at
+                               (row 0, col 0) and ends at (row 0, col n-1); the pattern is 1-D over
+                               the curve position */
+};
+
+/* Border rule of a pattern dimension. */
+enum {
+    NA_BOUND_CLAMP = 0,   /* the window is shifted to lie inside the axis (neighbourhood attention) */
+    NA_BOUND_TRUNCATE = 1 /* the window is cut at the axis ends (band / slide attention) */
+};
+
+enum { NA_BF16 = 0, NA_F32 = 1 };
+
+/* na_plan_create flags */
+#define NA_PLAN_HOST_ONLY 1u /* build the tile map on the host only: no device upload; the plan can
+                                be inspected but not run */
+
+/* na_forward flags */
+#define NA_FWD_PERMUTE_PASSES 1u /* for non-row-major orders: gather q, k, v into sequence order with
+                                    the permute kernel, attend on contiguous tiles, scatter out and
+                                    lse back (needs na_forward_workspace_bytes of workspace). Default:
+                                    the attention kernel gathers and scatters rows itself. */
+
+/*
+ * Plan descriptor.  Pattern dimensions are the grid dimensions, except for
+ * NA_ORDER_HILBERT where there is one pattern dimension: the curve position,
+ * of length N.  For pattern dimension d with length L, a query at coordinate x
+ * attends the keys y with
+ *     c   = (x' / stride) * stride + stride / 2       (x' = x / dilation)
+ *     lo  = c - left, hi = lo + window                 (left = window_left, or window / 2,
+ *                                                       or window - 1 when causal)
+ *     clamp:    [lo, hi) shifted to lie inside [0, L'), or all of [0, L') if window >= L'
+ *     truncate: [lo, hi) cut to [0, L')
+ * evaluated on the sub-grid of positions congruent to x modulo dilation (L' its length), and
+ * the N-D set is the Cartesian product of the per-dimension sets.  A causal dimension uses
+ * left = window - 1 and truncation.
+ */
+typedef struct {
+    int32_t ndim;           /* grid dimensions, 1..3 */
+    int32_t grid[3];        /* grid extents, slowest first; N = product, N < 2^31 */
+    int32_t order;          /* NA_ORDER_* */
+    int32_t tile[3];        /* NA_ORDER_TILED: tile extents (>= 1) */
+    int32_t window[3];      /* window length per pattern dimension (>= 1) */
+    int32_t window_left[3]; /* window start offset; -1 = window / 2 (window - 1 if causal) */
+    int32_t stride[3];      /* >= 1; 1 = plain sliding window */
+    int32_t dilation[3];    /* >= 1 */
+    int32_t causal[3];      /* 0 / 1 */
+    int32_t boundary[3];    /* NA_BOUND_* (ignored for causal dimensions) */
+    int32_t q_block;        /* query tile length in tokens, 0 = library default */
+    int32_t kv_block;       /* key/value tile length in tokens, 0 = library default */
+    int32_t head_dim;       /* D */
+    int32_t dtype;          /* NA_BF16 or NA_F32 */
+} na_plan_desc;
+
+typedef struct {
+    int64_t n_tokens;
+    int64_t q_block, kv_block;
+    int64_t n_q_tiles, n_kv_tiles;
+    int64_t n_empty, n_partial, n_full; /* over all n_q_tiles * n_kv_tiles pairs */
+    int64_t attended_pairs;             /* sum over queries of |neighbourhood|, per (batch, head) */
+} na_plan_stats;
+
+typedef struct {
+    void* ptr;                          /* device pointer to element [0, 0, 0, 0] */
+    int64_t stride_b, stride_h, stride_n; /* in elements; the D axis has stride 1 */
+} na_tensor;
+
+typedef struct na_plan_s* na_plan_t;
+
+/* Build a plan: validate the descriptor, build the token order, classify every
+ * (query tile, key/value tile) pair by interval arithmetic (exact: ambiguous
+ * pairs are counted element by element), store the non-empty pairs per query
+ * tile in CSR form, and (unless NA_PLAN_HOST_ONLY) upload order, CSR and the
+ * per-token mask tables to the current device.  The plan owns all of it and is
+ * immutable afterwards; it may be used from several streams at once.
+ * Returns NA_ERR_INVALID_ARG for a malformed descriptor, NA_ERR_UNSUPPORTED for
+ * a Hilbert order on a grid that is not a square power of two. */
+na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* plan);
+
+/* Release a plan (host and device memory).  The caller must first make sure
+ * that no enqueued work still uses it.  NULL is accepted. */
+na_status na_plan_destroy(na_plan_t plan);
+
+na_status na_plan_get_stats(na_plan_t plan, na_plan_stats* stats);
+
+/* Dense class matrix uint8 [n_q_tiles][n_kv_tiles]: 0 empty, 1 partial, 2 full.
+ * n must be at least n_q_tiles * n_kv_tiles. */
+na_status na_plan_get_classes(na_plan_t plan, uint8_t* host_classes, size_t n);
+
+/* perm[p] = row-major token at sequence position p; n must be >= N. */
+na_status na_plan_get_order(na_plan_t plan, int32_t* host_perm, size_t n);
+
+/* Workspace bytes na_forward needs for (B, H) with the given flags (0 for the
+ * default fused path). */
+size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t flags);
+
+/* out = softmax attention of q over its neighbourhood keys/values, lse as
+ * above.  q, k, v, out share the plan's dtype and head_dim; lse may be NULL.
+ * Returns NA_ERR_PLAN_MISMATCH if the plan was built host-only, and
+ * NA_ERR_UNSUPPORTED if no kernel matches (dtype, head_dim, q_block,
+ * kv_block): bf16 with head_dim 64 or 128 and (q_block, kv_block) =
+ * (128, 64) or (256, 64); fp32 with head_dim 32 or 64 and (32, 32). */
+na_status na_forward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
+                     const na_tensor* k, const na_tensor* v, const na_tensor* out, float* lse,
+                     float scale, uint32_t flags, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Row gather along the plan's order: out[b, h, p, :] = in[b, h, perm[p], :]
+ * (inverse = 0) or out[b, h, perm[p], :] = in[b, h, p, :] (inverse = 1), for
+ * the plan's dtype and head_dim.  in and out must not overlap. */
+na_status na_permute(na_plan_t plan, int64_t B, int64_t H, const na_tensor* in,
+                     const na_tensor* out, int32_t inverse, void* stream);
+
+const char* na_status_string(na_status status);
+const char* na_last_error(void);
+int32_t na_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

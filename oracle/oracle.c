@@ -122,10 +122,6 @@ static int64_t sta_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out) {
 }
 
 int64_t orc_rule_set(const orc_rule* r, int64_t len, int64_t x, int64_t* out) {
-    if (len <= 1) {
-        out[0] = 0;
-        return 1;
-    }
     switch (r->kind) {
         case ORC_WINDOW: return window_set(r, len, x, out);
         case ORC_BLOCKED: return blocked_set(r, len, x, out);

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances: fp32 max-abs 1e-5; bf16 max-abs 2e-2 and relative L2 5e-3 on the
+output.  LSE: 1e-5 (fp32) and 1e-3 (bf16): the scores are fp32 sums of exact
+bf16 products, so the LSE error is a few fp32 ulps of |scale * q.k|.
+Small cases compare every element; the full-size workloads compare sampled
+query rows (all grid corners plus seeded random rows), launched exactly as the
+benchmark launches them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from dimensional_sparse_local_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=1e-3)}
+
+
+def _na():
+    from dimensional_sparse_local_amd import na
+
+    if not os.path.exists(na._LIB_PATH):
+        raise RuntimeError("libna.so missing: the HIP path must be built")
+    return na
+
+
+def _check(wl, out, lse, ref_out, ref_lse, rows=None, label=""):
+    t = TOL[wl["dtype"]]
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        o = o[:, :, rows]
+        l = l[:, :, rows]
+    assert np.all(np.isfinite(o)), label
+    err = np.max(np.abs(o - ref_out))
+    assert err <= t["abs"], "%s: max-abs %.3e" % (label, err)
+    if t["rel"] is not None:
+        rel = np.linalg.norm(o - ref_out) / np.linalg.norm(ref_out)
+        assert rel <= t["rel"], "%s: rel-L2 %.3e" % (label, rel)
+    finite = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(l), finite), label
+    lerr = np.max(np.abs(l[finite] - ref_lse[finite])) if finite.any() else 0.0
+    assert lerr <= t["lse"], "%s: lse max-abs %.3e" % (label, lerr)
+    return err
+
+
+def _run(wl, rows=None, q_block=0, permute_passes=False, seed=None):
+    na = _na()
+    print("case %s grid=%s B=%d H=%d D=%d q_block=%d passes=%s" % (
+        wl["name"], wl["grid"], wl["B"], wl["H"], wl["D"], q_block, permute_passes), flush=True)
+    plan = na.Plan(wl, q_block=q_block)
+    q, k, v = W.make_qkv(wl, device="cuda", seed=seed)
+    scale = W.default_scale(wl)
+    out, lse = plan.forward(q, k, v, scale=scale, permute_passes=permute_passes)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention(wl, q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
+    return _check(wl, out, lse, ref_out, ref_lse, rows=rows, label=wl["name"])
+
+
+def _sample_rows(wl, n_random, seed=0):
+    grid = wl["grid"]
+    corners = set()
+    for c in np.ndindex(*([2] * len(grid))):
+        corners.add(int(np.ravel_multi_index([(g - 1) * b for g, b in zip(grid, c)], grid)))
+    rng = np.random.default_rng(seed)
+    rnd = rng.choice(W.num_tokens(wl), size=n_random, replace=False)
+    return np.array(sorted(corners | set(int(x) for x in rnd)), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# small cases: every element
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    W.CONFIGS["na2d_fp32"],
+    W.scaled(W.CONFIGS["na2d_fp32"], name="na2d_fp32_d64", D=64, grid=[9, 11], H=2,
+             pattern=dict(kind="na", window=[5, 3])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="na2d_bf16_small", B=1, H=2, grid=[24, 20],
+             pattern=dict(kind="na", window=[7, 5])),
+    W.scaled(W.CONFIGS["sta3d_bf16"], name="sta3d_small", H=2, grid=[12, 16, 24],
+             pattern=dict(kind="sta", tile=[6, 8, 8], window_tiles=[1, 1, 3])),
+    W.scaled(W.CONFIGS["sta3d_bf16"], name="sta3d_small_d64", H=1, D=64, grid=[6, 16, 40],
+             pattern=dict(kind="sta", tile=[6, 8, 8], window_tiles=[1, 1, 3])),
+    W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_small", B=2, H=2, grid=[32, 32],
+             pattern=dict(kind="band", left=37, right=37)),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="causal_small", H=2, grid=[1000],
+             pattern=dict(kind="band", left=99, right=0)),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="causal_small_d64", H=2, D=64, grid=[333],
+             pattern=dict(kind="band", left=70, right=0)),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="sa3d_ragged", B=1, H=1, grid=[5, 7, 9],
+             pattern=dict(kind="sa", window=[3, 5, 3])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="gna_stride_dil", B=1, H=2, grid=[19, 23],
+             pattern=dict(kind="na", window=[7, 5], stride=[3, 2], dilation=[2, 1])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="blocked_tiled", B=1, H=1, grid=[16, 16],
+             order="tiled", tile=[4, 8], pattern=dict(kind="blocked", window=[4, 8])),
+    W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_window", B=1, H=1, grid=[16, 16],
+             pattern=dict(kind="blocked", window=[16])),
+    W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_na", B=1, H=1, grid=[16, 16],
+             pattern=dict(kind="na", window=[25])),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w["name"] for w in SMALL])
+def test_small_full_compare(wl):
+    _run(wl)
+
+
+@pytest.mark.parametrize("q_block", [128, 256])
+def test_query_block_variants(q_block):
+    wl = W.scaled(W.CONFIGS["causal1d_bf16"], name="causal_qb", H=1, grid=[777],
+                  pattern=dict(kind="band", left=200, right=0))
+    _run(wl, q_block=q_block)
+
+
+def test_hilbert_permute_passes():
+    wl = W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_passes", B=1, H=3,
+                  grid=[32, 32], pattern=dict(kind="band", left=40, right=40))
+    _run(wl, permute_passes=True)
+
+
+def test_dense_window_equals_dense_attention():
+    wl = W.scaled(W.CONFIGS["na2d_bf16"], name="dense", B=1, H=2, grid=[10, 13],
+                  pattern=dict(kind="na", window=[10, 13]))
+    _run(wl)
+
+
+def test_one_token_window_is_v():
+    na = _na()
+    wl = W.scaled(W.CONFIGS["na2d_bf16"], name="one", B=1, H=2, grid=[9, 15],
+                  pattern=dict(kind="na", window=[1, 1]))
+    plan = na.Plan(wl)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    out, lse = plan.forward(q, k, v, scale=0.125)
+    assert torch.equal(out, v)
+    want = 0.125 * (q.float() * k.float()).sum(-1)
+    assert torch.max(torch.abs(lse - want)).item() < 1e-4
+
+
+def test_empty_rows():
+    """A window that excludes the query itself leaves the first rows empty:
+    out = 0, lse = -inf."""
+    na = _na()
+    wl = W.scaled(W.CONFIGS["causal1d_bf16"], name="strict_past", H=1, grid=[300],
+                  pattern=dict(kind="band", left=10, right=0))
+    d = na.desc_from_workload(wl)
+    d.window[0] = 10
+    d.window_left[0] = 10          # keys [x - 10, x - 1]
+    plan = na.Plan(d)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    out, lse = plan.forward(q, k, v, scale=0.1)
+    assert torch.all(out[:, :, 0] == 0) and torch.isinf(lse[:, :, 0]).all()
+    ref_wl = W.scaled(wl, pattern=dict(kind="band", left=10, right=-1))
+    ref_out, ref_lse = oracle.attention(ref_wl, q.cpu(), k.cpu(), v.cpu(), 0.1)
+    _check(wl, out, lse, ref_out, ref_lse, label="strict_past")
+
+
+def test_strided_views_and_poison():
+    na = _na()
+    wl = W.scaled(W.CONFIGS["na2d_bf16"], name="views", B=2, H=3, grid=[12, 12],
+                  pattern=dict(kind="na", window=[5, 5]))
+    plan = na.Plan(wl)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    # [B, N, H, D] storage viewed as [B, H, N, D]
+    qs, ks, vs = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    out = torch.full((2, 144, 3, 64), float("nan"), dtype=torch.bfloat16,
+                     device="cuda").transpose(1, 2)
+    lse = torch.full((2, 3, 144), float("nan"), device="cuda")
+    plan.forward(qs, ks, vs, out=out, lse=lse, scale=0.125)
+    ref, ref_lse = plan.forward(q, k, v, scale=0.125)
+    assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+    assert not torch.isnan(out).any()
+
+
+def test_deterministic():
+    na = _na()
+    wl = W.scaled(W.CONFIGS["hilbert_band_bf16"], name="det", B=1, H=2, grid=[32, 32],
+                  pattern=dict(kind="band", left=50, right=50))
+    plan = na.Plan(wl)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    a, la = plan.forward(q, k, v)
+    for _ in range(3):
+        b, lb = plan.forward(q, k, v)
+        assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_permute_roundtrip():
+    na = _na()
+    wl = W.scaled(W.CONFIGS["hilbert_band_bf16"], name="perm", B=2, H=3, grid=[64, 64])
+    plan = na.Plan(wl)
+    q, _, _ = W.make_qkv(wl, device="cuda")
+    perm = torch.from_numpy(oracle.hilbert(64)).cuda()
+    fwd = plan.permute(q)
+    assert torch.equal(fwd, q[:, :, perm])
+    back = plan.permute(fwd, inverse=True)
+    assert torch.equal(back, q)
+
+
+def test_abi_rejects_bad_tensors():
+    na = _na()
+    wl = W.scaled(W.CONFIGS["na2d_bf16"], name="bad", B=1, H=1, grid=[8, 8])
+    plan = na.Plan(wl)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    with pytest.raises(ValueError):
+        plan.forward(q.float(), k, v)
+    good = na.Tensor(q.data_ptr(), q.stride(0), q.stride(1), q.stride(2))
+    bad = na.Tensor(q.data_ptr() + 2, q.stride(0), q.stride(1), q.stride(2))
+    out = torch.empty_like(q)
+    o = na.Tensor(out.data_ptr(), out.stride(0), out.stride(1), out.stride(2))
+    st = na.lib().na_forward(plan._h, 1, 1, bad, good, good, o, None, 0.1, 0, None, 0, None)
+    assert st == na.NA_ERR_INVALID_ARG
+    st = na.lib().na_forward(plan._h, 1, 1, good, good, good, o, None, float("nan"), 0, None, 0,
+                             None)
+    assert st == na.NA_ERR_INVALID_ARG
+    d = na.desc_from_workload(W.scaled(wl, D=96))
+    p96 = na.Plan(d)
+    q96 = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(na.NaError) as ei:
+        p96.forward(q96, q96, q96)
+    assert ei.value.status == na.NA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled rows, launched as the benchmark launches them
+# ---------------------------------------------------------------------------
+
+FULL = [("na2d_fp32", None), ("na2d_bf16", None), ("sta3d_bf16", 24),
+        ("hilbert_band_bf16", 192), ("causal1d_bf16", 96)]
+
+
+@pytest.mark.parametrize("name,n_rows", FULL, ids=[f[0] for f in FULL])
+def test_full_size(name, n_rows):
+    wl = W.CONFIGS[name]
+    rows = None if n_rows is None else _sample_rows(wl, n_rows, seed=wl["seed"])
+    _run(wl, rows=rows)

@@ -1,0 +1,199 @@
+"""Host planner (through the C ABI, host-only plans) against the oracle.
+
+Tile classes must match bit for bit; orders, pair counts and class counts
+exactly.  No GPU is needed: plans are built with NA_PLAN_HOST_ONLY.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from dimensional_sparse_local_amd import na
+from dimensional_sparse_local_amd import workloads as W
+
+pytestmark = pytest.mark.skipif(not os.path.exists(na._LIB_PATH), reason="libna.so not built")
+
+
+def _plan(wl, qb, kb, D=64, dtype="bf16"):
+    wl = dict(wl)
+    wl.setdefault("D", D)
+    wl.setdefault("dtype", dtype)
+    return na.Plan(wl, host_only=True, q_block=qb, kv_block=kb)
+
+
+def _compare(wl, qb, kb):
+    p = _plan(wl, qb, kb)
+    want, pairs = oracle.tile_classes(wl, qb, kb)
+    got = p.classes()
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), "tile classes differ at %s" % (
+        np.argwhere(got != want)[:5].tolist(),)
+    st = p.stats
+    assert st["attended_pairs"] == pairs
+    assert (st["n_empty"], st["n_partial"], st["n_full"]) == tuple(
+        int((want == c).sum()) for c in range(3))
+    assert np.array_equal(p.order().astype(np.int64), oracle.order(wl))
+    return p
+
+
+@pytest.mark.parametrize("name", ["na2d_fp32", "na2d_bf16", "hilbert_band_bf16", "causal1d_bf16"])
+def test_config_tile_maps(name):
+    wl = W.CONFIGS[name]
+    p = na.Plan(wl, host_only=True)           # library default blocks
+    qb, kb = p.stats["q_block"], p.stats["kv_block"]
+    _compare(wl, qb, kb)
+    for qb2, kb2 in [(128, 64), (256, 64), (16, 16)]:
+        if oracle.num_tokens(wl) <= 20000:
+            _compare(wl, qb2, kb2)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("qb", [128, 256])
+def test_config_tile_map_sta(qb):
+    wl = W.CONFIGS["sta3d_bf16"]
+    p = _compare(wl, qb, 64)
+    st = p.stats
+    assert st["attended_pairs"] == 115200 * 40320
+    if 384 % qb == 0:
+        # query block divides the 6x8x8 tile: no partial tiles, 105 of 300
+        # tiles attended by every query tile (35%)
+        assert st["n_partial"] == 0
+        assert st["n_full"] == (115200 // qb) * (105 * 384 // 64)
+    else:
+        # a query block straddling two tiles sees the union of their windows
+        assert st["n_partial"] > 0
+
+
+def test_config_class_counts():
+    # the counts recorded for the benchmark workloads at the default blocks
+    expect = {"na2d_bf16": (1606, 442, 0, 692224),
+              "hilbert_band_bf16": (31500, 504, 764, 8339200),
+              "causal1d_bf16": (115232, 960, 14880, 125831168)}
+    for name, (e, p_, f, pairs) in expect.items():
+        st = na.Plan(W.CONFIGS[name], host_only=True).stats
+        assert (st["n_empty"], st["n_partial"], st["n_full"], st["attended_pairs"]) == \
+            (e, p_, f, pairs), name
+
+
+def test_page_tables_through_planner(golden_dir):
+    data = json.load(open(os.path.join(golden_dir, "hilbert_block_sparsity.json")))
+    for case in data["cases"]:
+        wl = dict(grid=case["grid"], order=case["order"], pattern=case["pattern"])
+        p = _compare(wl, case["block"], case["block"])
+        pct = 100.0 * p.stats["n_empty"] / (p.stats["n_q_tiles"] * p.stats["n_kv_tiles"])
+        assert round(pct, 2) == case["empty_pct"], case["label"]
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 64, 128, 256])
+def test_hilbert_order_matches_oracle(n):
+    wl = dict(grid=[n, n], order="hilbert", pattern=dict(kind="band", left=1, right=1))
+    p = _plan(wl, 16, 16)
+    assert np.array_equal(p.order().astype(np.int64), oracle.hilbert(n))
+
+
+def _random_workload(rng):
+    kind = rng.choice(["na", "sa", "band", "blocked", "sta", "hilbert"])
+    if kind == "band":
+        n = int(rng.integers(1, 300))
+        left, right = int(rng.integers(0, 40)), int(rng.integers(0, 40))
+        return dict(grid=[n], pattern=dict(kind="band", left=left, right=right))
+    if kind == "hilbert":
+        n = int(2 ** rng.integers(1, 5))
+        sub = rng.choice(["band", "blocked", "na"])
+        if sub == "band":
+            r = int(rng.integers(0, 20))
+            pat = dict(kind="band", left=r, right=int(rng.integers(0, 20)))
+        elif sub == "blocked":
+            pat = dict(kind="blocked", window=[int(rng.integers(1, 20))])
+        else:
+            pat = dict(kind="na", window=[int(rng.integers(1, 30))])
+        return dict(grid=[n, n], order="hilbert", pattern=pat)
+    ndim = int(rng.integers(1, 4))
+    grid = [int(rng.integers(1, 12)) for _ in range(ndim)]
+    if kind == "sta":
+        tile = [int(rng.integers(1, 4)) for _ in range(ndim)]
+        grid = [t * int(rng.integers(1, 5)) for t in tile]
+        wt = [int(rng.integers(1, 4)) for _ in range(ndim)]
+        order = "tiled" if rng.random() < 0.7 else "row_major"
+        return dict(grid=grid, order=order, tile=tile,
+                    pattern=dict(kind="sta", tile=tile, window_tiles=wt))
+    window = [int(rng.integers(1, g + 3)) for g in grid]
+    pat = dict(kind=kind, window=window)
+    if kind in ("na", "sa"):
+        pat["stride"] = [int(rng.integers(1, min(3, w) + 1)) for w in window]
+        pat["dilation"] = [int(rng.integers(1, 3)) for _ in grid]
+    wl = dict(grid=grid, pattern=pat)
+    if rng.random() < 0.3:
+        wl["order"] = "tiled"
+        wl["tile"] = [int(rng.integers(1, 4)) for _ in grid]
+    return wl
+
+
+def test_random_tiny_workloads():
+    rng = np.random.default_rng(1234)
+    for it in range(300):
+        wl = _random_workload(rng)
+        n = oracle.num_tokens(wl)
+        qb = int(rng.integers(1, max(2, n // 2 + 2)))
+        kb = int(rng.integers(1, max(2, n // 2 + 2)))
+        try:
+            _compare(wl, qb, kb)
+        except AssertionError as e:
+            raise AssertionError("workload %r qb=%d kb=%d: %s" % (wl, qb, kb, e))
+
+
+def test_hilbert_non_power_of_two_unsupported():
+    wl = dict(grid=[96, 96], order="hilbert", pattern=dict(kind="band", left=5, right=5),
+              D=64, dtype="bf16")
+    with pytest.raises(na.NaError) as ei:
+        na.Plan(wl, host_only=True)
+    assert ei.value.status == na.NA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("field,value", [
+    ("ndim", 0), ("ndim", 4), ("grid", [0, 4, 1]), ("order", 7), ("dtype", 9), ("head_dim", 0),
+    ("window", [0, 3, 1]), ("stride", [3, 0, 1]), ("dilation", [1, 0, 1]), ("causal", [2, 0, 0]),
+    ("boundary", [5, 0, 0]), ("window_left", [-3, -1, -1]), ("q_block", -1), ("kv_block", -5),
+    ("stride", [4, 1, 1]),
+])
+def test_invalid_descriptors(field, value):
+    d = na.desc_from_workload(dict(grid=[4, 4], pattern=dict(kind="na", window=[3, 3]), D=64,
+                                   dtype="bf16"))
+    if isinstance(value, list):
+        for i, x in enumerate(value):
+            getattr(d, field)[i] = x
+    else:
+        setattr(d, field, value)
+    with pytest.raises(na.NaError) as ei:
+        na.Plan(d, host_only=True)
+    assert ei.value.status == na.NA_ERR_INVALID_ARG
+
+
+def test_tiled_needs_tiles():
+    d = na.desc_from_workload(dict(grid=[4, 4], order="tiled", tile=[2, 2],
+                                   pattern=dict(kind="na", window=[3, 3]), D=64, dtype="bf16"))
+    d.tile[1] = 0
+    with pytest.raises(na.NaError) as ei:
+        na.Plan(d, host_only=True)
+    assert ei.value.status == na.NA_ERR_INVALID_ARG
+
+
+def test_causal_flag_equals_left_extent():
+    base = dict(grid=[200], D=64, dtype="bf16")
+    a = na.desc_from_workload(dict(base, pattern=dict(kind="band", left=19, right=0)))
+    b = na.desc_from_workload(dict(base, pattern=dict(kind="na", window=[20])))
+    b.causal[0] = 1
+    pa, pb = na.Plan(a, host_only=True), na.Plan(b, host_only=True)
+    assert np.array_equal(pa.classes(), pb.classes())
+    assert pa.stats == pb.stats
+
+
+def test_host_only_plan_cannot_run():
+    torch = pytest.importorskip("torch")
+    p = na.Plan(W.CONFIGS["na2d_bf16"], host_only=True)
+    t = na.Tensor(16, 0, 0, 64)
+    st = na.lib().na_forward(p._h, 1, 1, t, t, t, t, None, 0.1, 0, None, 0, None)
+    assert st == na.NA_ERR_PLAN_MISMATCH
+    del torch
