@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--permute-passes", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only the row-permute kernel over 268,435,456 bytes (read once, "
+                         "written once): the known-size copy that calibrates HBM counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -107,6 +110,19 @@ def main():
 
     from dimensional_sparse_local_amd import na
     from dimensional_sparse_local_amd import workloads as W
+
+    if args.copy_probe:
+        wl = dict(name="copy_probe", B=1, H=4, D=128, dtype="bf16", grid=[512, 512],
+                  order="hilbert", pattern=dict(kind="band", left=1, right=1), seed=0)
+        plan = na.Plan(wl)
+        x = W.make_qkv(wl, device="cuda:0")[0]
+        y = torch.empty_like(x)
+        for _ in range(3):
+            plan.permute(x, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": x.numel() * 2,
+                          "copy_probe_bytes_written": y.numel() * 2, "launches": 3}))
+        return
 
     name = args.workload or W.HEADLINE
     wl = W.CONFIGS[name]

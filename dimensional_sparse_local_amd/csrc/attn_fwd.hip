@@ -31,73 +31,151 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// fp32 -> bf16, round to nearest even (NaN preserved).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Load through a global-address-space pointer (a flat load would also count
+// against the LDS wait counter).
+template <typename T>
+__device__ __forceinline__ T gload(const T* ptr) {
+    return *(const __attribute__((address_space(1))) T*)(ptr);
 }
 
-__device__ __forceinline__ bf16x8 pack8(const float* v) {
-    u32x4 w;
-    w[0] = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-    w[1] = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-    w[2] = bf16_bits(v[4]) | (bf16_bits(v[5]) << 16);
-    w[3] = bf16_bits(v[6]) | (bf16_bits(v[7]) << 16);
+// Load of read-only, wave-uniform data through the constant address space
+// (a scalar load).
+template <typename T>
+__device__ __forceinline__ T cload(const T* ptr) {
+    return *(const __attribute__((address_space(4))) T*)(ptr);
+}
+
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ NaEntry load_entry(const NaEntry* e) {
+    const i32x2 v = cload((const i32x2*)e);
+    return NaEntry{v[0], v[1]};
+}
+
+// Keep score x when bit `bit` of word w is set, else -inf.
+__device__ __forceinline__ float keep_if(uint32_t w, int bit, float x) {
+    return (w >> bit) & 1u ? x : kNegInf;
+}
+
+// ---------------------------------------------------------------------------
+// bf16: NW waves of 32 queries each (query tile 32*NW), key/value tile 64.
+//
+// Two waves share every SIMD (<= 256 registers each), so the MFMA phase of one
+// overlaps the softmax phase of the other.  K and V tiles travel from HBM/L2
+// straight into LDS (global_load_lds, 16 bytes per lane, no register staging)
+// into two statically selected buffers: while tile e is computed from one
+// buffer, tile e+1 streams into the other.  The gather addresses are prepared
+// ahead: the CSR entry of tile e+3 and the token indices of tile e+2 are
+// fetched while tile e is computed, so no dependent load stalls a step.
+//
+// LDS rows of K and V are padded by one 16-byte chunk (row stride D + 8
+// elements); the DMA fills the pad slots from a zero page, so one DMA block of
+// 64 lanes covers 64 consecutive (row, chunk) slots and K and V share one slot
+// -> row map.  Both operand reads are bank-conflict free at this stride: the K
+// operand reads one chunk from each of 16 consecutive rows per 16-lane phase,
+// and each V^T transpose read takes rows {0, 2, 8, 10} or {1, 3, 9, 11} (+4
+// per half, +16 per step) of the tile, whose 32-byte segments fall on disjoint
+// banks; the P^T operand slots follow the same row order.
+//
+// Online softmax in the log2 domain with a lazy rescale: a row's reference
+// maximum moves (and O, l are rescaled) only when the tile maximum exceeds it
+// by more than 2^8, which keeps every P <= 256 and is exact after the final
+// division by l.
+// ---------------------------------------------------------------------------
+constexpr float kRescaleLog2 = 8.0f;
+
+typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)(lds), 16, 0, 0);
+}
+
+// Wait for all of this wave's vector memory operations (including LDS DMA).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                       float a6, float a7) {
+    const f32x2 x0 = {a0, a1}, x1 = {a2, a3}, x2 = {a4, a5}, x3 = {a6, a7};
+    const bf16x2 y0 = __builtin_convertvector(x0, bf16x2);
+    const bf16x2 y1 = __builtin_convertvector(x1, bf16x2);
+    const bf16x2 y2 = __builtin_convertvector(x2, bf16x2);
+    const bf16x2 y3 = __builtin_convertvector(x3, bf16x2);
+    u32x4 w = {__builtin_bit_cast(uint32_t, y0), __builtin_bit_cast(uint32_t, y1),
+               __builtin_bit_cast(uint32_t, y2), __builtin_bit_cast(uint32_t, y3)};
     return __builtin_bit_cast(bf16x8, w);
 }
 
-// Window test of one key (pattern coordinates kc) against a query box
-// (lo[3], hi[3]); dilation: the key must sit on the query's sub-grid.
-__device__ __forceinline__ bool in_window(const int32_t* lo, const int32_t* hi, int4 kc,
-                                          const NaAttnParams& p) {
-    bool ok = kc.x >= lo[0] && kc.x < hi[0];
-    if (p.pdims > 1) ok = ok && kc.y >= lo[1] && kc.y < hi[1];
-    if (p.pdims > 2) ok = ok && kc.z >= lo[2] && kc.z < hi[2];
-    if (p.has_dilation) {
-        ok = ok && (kc.x - lo[0]) % p.dil0 == 0;
-        if (p.pdims > 1) ok = ok && (kc.y - lo[1]) % p.dil1 == 0;
-        if (p.pdims > 2) ok = ok && (kc.z - lo[2]) % p.dil2 == 0;
-    }
-    return ok;
+// Combine a value across the two half-waves (lanes l and l ^ 32).  The swap
+// returns {this lane's vdst, this lane's vsrc}; the partner's value sits in
+// the first for lanes 0-31 and in the second for lanes 32-63, and the other
+// element holds the lane's own value, so a symmetric reduction of the pair is
+// the same on every lane.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// ---------------------------------------------------------------------------
-// bf16: NW waves, 32 queries per wave (query tile 32*NW), key/value tile 64.
-// ---------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16(NaAttnParams p) {
-    constexpr int KV = NA_KV_BLOCK_BF16;
-    constexpr int NT = NW * 64;
-    constexpr int QB = 32 * NW;
-    constexpr int ROW = D + 8;                 // LDS row stride (elements): 16 B pad
-    constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int CH = KV * CPR / NT;          // chunks per thread per tensor
-    static_assert(KV * CPR % NT == 0, "tile does not split evenly");
-    constexpr int KS = D / 16;                 // QK reduction steps
-    constexpr int DB = D / 32;                 // PV output blocks
+// Workgroup index -> logical tile index.  Workgroups are dispatched to the 8
+// XCDs round-robin; give each XCD one contiguous range of logical tiles
+// (consecutive query tiles of one head) so that the tiles sharing key/value
+// tiles share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    constexpr int kXcd = 8;
+    const int q = n / kXcd, r = n % kXcd;
+    const int x = bid % kXcd, local = bid / kXcd;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[KV * ROW];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[KV * ROW];
-    __shared__ int4 kc_lds[KV];
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16(NaAttnParams p) {
+    constexpr int KV = NA_KV_BLOCK_BF16;
+    constexpr int QB = 32 * NW;
+    constexpr int ROW = D + 8;                   // padded LDS row (elements)
+    constexpr int CS = D / 8 + 1;                // 16-byte slots per padded row
+    constexpr int TILE = KV * ROW;               // LDS elements per tensor tile
+    constexpr int NI = CS;                       // 1 KB DMA blocks per tensor tile (64*CS slots)
+    constexpr int IPW = (NI + NW - 1) / NW;      // DMA blocks per wave (the last may be idle)
+    constexpr int KS = D / 16;                   // QK reduction steps
+    constexpr int DB = D / 32;                   // PV output blocks
+
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
 
-    const int wg = blockIdx.x;
+    const int wg = xcd_remap(blockIdx.x, p.n_wg);
     const int qt = wg % p.n_q_tiles;
     const int bh = wg / p.n_q_tiles;
     const int b = bh / p.heads, h = bh % p.heads;
     const int N = p.n_tokens;
+    const float c = p.scale_log2;
 
     // ---- this lane's query -------------------------------------------------
     const int qpos = qt * QB + wave * 32 + l32;
@@ -105,7 +183,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16(NaAttnParams p) {
     const int qtok = qvalid ? (p.perm ? p.perm[qpos] : qpos) : 0;
     bf16x8 qf[KS];
     {
-        const uint16_t* qrow = (const uint16_t*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qtok * p.q_sn;
+        const uint16_t* qrow =
+            (const uint16_t*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qtok * p.q_sn;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             u32x4 w = {0u, 0u, 0u, 0u};
@@ -113,50 +192,52 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16(NaAttnParams p) {
             qf[s] = __builtin_bit_cast(bf16x8, w);
         }
     }
-    int32_t qlo[3] = {0, 0, 0}, qhi[3] = {0, 0, 0};
-    if (p.qbox && qvalid) {
-        const int4 a = *(const int4*)(p.qbox + (int64_t)qpos * 8);
-        const int4 c = *(const int4*)(p.qbox + (int64_t)qpos * 8 + 4);
-        qlo[0] = a.x; qlo[1] = a.y; qlo[2] = a.z;
-        qhi[0] = a.w; qhi[1] = c.x; qhi[2] = c.y;
-    }
-
     const uint16_t* kbase = (const uint16_t*)p.k + b * p.k_sb + h * p.k_sh;
     const uint16_t* vbase = (const uint16_t*)p.v + b * p.v_sb + h * p.v_sh;
+    // this lane's row of a tile mask (two 32-key words)
+    const int mrow = wave * 32 + l32;
 
-    // ---- register staging of one key/value tile ----------------------------
-    u32x4 kreg[CH], vreg[CH];
-    int4 kcreg = {0, 0, 0, 0};
-    auto load_tile = [&](uint32_t entry) {
-        const int kt = (int)(entry & ~NA_ENTRY_PARTIAL);
+    // DMA block j = wave + NW*i moves slots 64*j .. 64*j+63 of a tile; lane t
+    // moves slot 64*j + t = (row, chunk) with CS slots per row; chunk CS-1 is
+    // the pad and comes from the zero page.
+    int dma_row[IPW], dma_ch[IPW];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + NT * i;
-            const int row = c / CPR, col = (c % CPR) * 8;
-            const int kp = kt * KV + row;
-            u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-            if (kp < N) {
-                const int tok = p.perm ? p.perm[kp] : kp;
-                kw = *(const u32x4*)(kbase + (int64_t)tok * p.k_sn + col);
-                vw = *(const u32x4*)(vbase + (int64_t)tok * p.v_sn + col);
-            }
-            kreg[i] = kw;
-            vreg[i] = vw;
-        }
-        if ((entry & NA_ENTRY_PARTIAL) && tid < KV) {
-            const int kp = kt * KV + tid;
-            kcreg = kp < N ? *(const int4*)(p.kcoord + (int64_t)kp * 4) : int4{0, 0, 0, 0};
+    for (int i = 0; i < IPW; ++i) {
+        const int slot = 64 * (wave + NW * i) + lane;
+        dma_row[i] = slot / CS;
+        dma_ch[i] = slot % CS;
+    }
+    // Token of the row this lane moves in each of its DMA blocks, fetched one
+    // step ahead.  The order lookup is unconditional (clamped index) and its
+    // value is not used before the DMA is issued, so fetching it never waits.
+    auto tokens = [&](NaEntry entry, int* tok) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int kp = entry.kt * KV + dma_row[i];
+            tok[i] = p.perm ? gload(p.perm + (kp < N ? kp : N - 1)) : kp;
         }
     };
-    auto store_tile = [&](uint32_t entry) {
+    auto issue = [&](NaEntry entry, const int* tok, uint16_t* kl, uint16_t* vl) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + NT * i;
-            const int row = c / CPR, col = (c % CPR) * 8;
-            *(u32x4*)(k_lds + row * ROW + col) = kreg[i];
-            *(u32x4*)(v_lds + row * ROW + col) = vreg[i];
+        for (int i = 0; i < IPW; ++i) {
+            const int blk = wave + NW * i;
+            if (blk < NI) {  // wave-uniform
+                const bool real = dma_ch[i] < CS - 1 && entry.kt * KV + dma_row[i] < N;
+                const int ch = dma_ch[i] < CS - 1 ? dma_ch[i] : 0;
+                const uint16_t* gk = real ? kbase + (int64_t)tok[i] * p.k_sn + 8 * ch
+                                          : (const uint16_t*)p.zero;
+                const uint16_t* gv = real ? vbase + (int64_t)tok[i] * p.v_sn + 8 * ch
+                                          : (const uint16_t*)p.zero;
+                dma16(gk, kl + blk * 512);
+                dma16(gv, vl + blk * 512);
+            }
         }
-        if ((entry & NA_ENTRY_PARTIAL) && tid < KV) kc_lds[tid] = kcreg;
+    };
+    auto mask_row = [&](NaEntry entry) {
+        u32x2 w = {0u, 0u};
+        if (entry.mask >= 0)
+            w = gload((const u32x2*)(p.masks + ((int64_t)entry.mask * QB + mrow) * 2));
+        return w;
     };
 
     f32x16 o[DB];
@@ -164,97 +245,134 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16(NaAttnParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    float m_run = kNegInf, l_run = 0.f;
+    float m_ref = kNegInf;   // reference maximum (log2 domain) of O and l
+    float l_run = 0.f;
 
-    const int e0 = p.row_ptr[qt], e1 = p.row_ptr[qt + 1];
-    if (e0 < e1) load_tile(p.entries[e0]);
-    for (int e = e0; e < e1; ++e) {
-        const uint32_t entry = p.entries[e];
-        store_tile(entry);
-        __syncthreads();
-        if (e + 1 < e1) load_tile(p.entries[e + 1]);
+    // V^T transpose-read addressing: in 16-lane group g = lane/16 the source
+    // lane s = lane%16 supplies slot s/4 of its group: row 16*ks + 4*half +
+    // {0, 2, 8, 10}[s/4] (first read) or that + 1 (second read), element column
+    // 32*db + 16*(g%2) + 4*(s%4).
+    const int tr_slot = (lane & 15) >> 2;
+    const int tr_base = (4 * half + 2 * (tr_slot & 1) + 8 * (tr_slot >> 1)) * ROW +
+                        16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-        const int kt = (int)(entry & ~NA_ENTRY_PARTIAL);
+    auto compute = [&](NaEntry entry, u32x2 mk, const uint16_t* kl, const uint16_t* vl) {
         // S^T = K Q^T for the two 32-key halves of the tile.
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            const uint16_t* kr = kl + (32 * kb + l32) * ROW + 8 * half;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *(const bf16x8*)(k_lds + (32 * kb + l32) * ROW + 16 * ks + 8 * half);
+                const bf16x8 a = *(const bf16x8*)(kr + 16 * ks);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
             }
         }
-        // scale into the log2 domain; mask if partial or ragged
-        const bool partial = (entry & NA_ENTRY_PARTIAL) != 0;
-        const bool ragged = kt * KV + KV > N;
-        float mt = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        // element mask (partial tiles and tiles past the last key only): score
+        // (kb, r) is key 32*kb + 8*(r/4) + 4*half + r%4 of the tile
+        if (entry.mask >= 0) {
+            const uint32_t w0 = mk[0] >> (4 * half), w1 = mk[1] >> (4 * half);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = s[kb][r] * p.scale_log2;
-                if (partial || ragged) {
-                    const int key = 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
-                    bool ok = kt * KV + key < N;
-                    if (partial && ok) ok = in_window(qlo, qhi, kc_lds[key], p);
-                    x = ok ? x : kNegInf;
-                }
-                s[kb][r] = x;
-                mt = fmaxf(mt, x);
+                s[0][r] = keep_if(w0, 8 * (r / 4) + (r % 4), s[0][r]);
+                s[1][r] = keep_if(w1, 8 * (r / 4) + (r % 4), s[1][r]);
             }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-        l_run *= alpha;
+        }
+        float mx = kNegInf;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+        mx = halves_max(mx);
+        const float m_tile = mx * c;
+        const bool grow = m_tile > m_ref + kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            // rows that do not grow keep alpha = 1 (their m_ref may still be -inf)
+            const float m_new = grow ? m_tile : m_ref;
+            const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+        const float neg_m = m_ref == kNegInf ? 0.f : -m_ref;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pe = fast_exp2(s[kb][r] - m_use);
+                const float pe = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
                 s[kb][r] = pe;
                 l_run += pe;
             }
-        // O^T += V^T P^T, 16 keys per step: P^T slot j of half h is the score
-        // of key 16*ks + 8*(j/4) + 4*h + j%4, i.e. accumulator elements
-        // 8*(ks%2)..+7 of block ks/2.
+        // O^T += V^T P^T, 16 keys per step.  Step ks covers accumulator
+        // elements r0 = 8*(ks%2) .. r0+7 of score block ks/2 (tile rows
+        // 16*ks + 4*half + {0..3, 8..11}); P^T slots take them in the order
+        // r0 + {0, 2, 4, 6, 1, 3, 5, 7}, matching the rows of the two
+        // transpose reads.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            float pv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pv[j] = s[ks / 2][8 * (ks % 2) + j];
-            const bf16x8 bp = pack8(pv);
+            const f32x16& sv = s[ks / 2];
+            const int r0 = 8 * (ks % 2);
+            const bf16x8 bp = cvt8(sv[r0], sv[r0 + 2], sv[r0 + 4], sv[r0 + 6], sv[r0 + 1],
+                                   sv[r0 + 3], sv[r0 + 5], sv[r0 + 7]);
+            const uint16_t* vr = vl + tr_base + 16 * ks * ROW;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int d = 32 * db + l32;
-                uint16_t va[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int key = 16 * ks + 8 * (j / 4) + 4 * half + (j % 4);
-                    va[j] = v_lds[key * ROW + d];
-                }
-                u32x4 w;
-                w[0] = va[0] | ((uint32_t)va[1] << 16);
-                w[1] = va[2] | ((uint32_t)va[3] << 16);
-                w[2] = va[4] | ((uint32_t)va[5] << 16);
-                w[3] = va[6] | ((uint32_t)va[7] << 16);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), bp,
-                                                                o[db], 0, 0, 0);
+                const bf16x4 lo = lds_read_tr(vr + 32 * db);
+                const bf16x4 hi = lds_read_tr(vr + ROW + 32 * db);
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[db], 0, 0, 0);
             }
         }
+    };
+
+    // ---- pipelined walk over the CSR row ------------------------------------
+    // Entering step e: tile e is in flight to (or in) its LDS buffer, ent_a..c
+    // are the entries of tiles e..e+2, tok_n the tokens of tile e+1 and mk_a /
+    // mk_b the mask rows of tiles e / e+1.
+    const int e0 = cload(p.row_ptr + qt), e1 = cload(p.row_ptr + qt + 1);
+    const NaEntry none = {0, -1};
+    NaEntry ent_a = none, ent_b = none, ent_c = none;
+    int tok_n[IPW];
+    u32x2 mk_a = {0u, 0u}, mk_b = {0u, 0u};
+    if (e0 < e1) {
+        ent_a = load_entry(p.entries + e0);
+        if (e0 + 1 < e1) ent_b = load_entry(p.entries + e0 + 1);
+        if (e0 + 2 < e1) ent_c = load_entry(p.entries + e0 + 2);
+        int tok0[IPW];
+        tokens(ent_a, tok0);
+        issue(ent_a, tok0, k_lds0, v_lds0);
+        mk_a = mask_row(ent_a);
+        if (e0 + 1 < e1) {
+            tokens(ent_b, tok_n);
+            mk_b = mask_row(ent_b);
+        }
+    }
+    auto step = [&](int e, const uint16_t* kl, const uint16_t* vl, uint16_t* kn, uint16_t* vn) {
+        wait_vmem();
         __syncthreads();
+        if (e + 1 < e1) issue(ent_b, tok_n, kn, vn);
+        if (e + 2 < e1) tokens(ent_c, tok_n);
+        const u32x2 mk_c = e + 2 < e1 ? mask_row(ent_c) : u32x2{0u, 0u};
+        const NaEntry ent_d = e + 3 < e1 ? load_entry(p.entries + e + 3) : none;
+        compute(ent_a, mk_a, kl, vl);
+        ent_a = ent_b;
+        ent_b = ent_c;
+        ent_c = ent_d;
+        mk_a = mk_b;
+        mk_b = mk_c;
+    };
+    for (int e = e0; e < e1; e += 2) {
+        step(e, k_lds0, v_lds0, k_lds1, v_lds1);
+        if (e + 1 < e1) step(e + 1, k_lds1, v_lds1, k_lds0, v_lds0);
     }
 
     // ---- epilogue -----------------------------------------------------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = halves_sum(l_run);
     if (!qvalid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = (uint16_t*)p.out + b * p.o_sb + h * p.o_sh + (int64_t)qtok * p.o_sn;
@@ -263,13 +381,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16(NaAttnParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = 32 * db + 8 * g + 4 * half;
-            u16x4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = (uint16_t)bf16_bits(o[db][4 * g + i] * inv);
-            *(u16x4*)(orow + d) = w;
+            const f32x2 x0 = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv};
+            const f32x2 x1 = {o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+            const uint2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(x0, bf16x2)),
+                             __builtin_bit_cast(uint32_t, __builtin_convertvector(x1, bf16x2))};
+            *(uint2*)(orow + d) = w;
         }
     if (p.lse && half == 0) {
-        const float lse = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+        const float lse = l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
         p.lse[(int64_t)bh * N + qtok] = lse;
     }
 }
@@ -285,7 +404,6 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(NaAttnParams p) {
     constexpr int DB = D / 32;
     __shared__ float k_lds[KV * ROW];
     __shared__ float v_lds[KV * ROW];
-    __shared__ int4 kc_lds[KV];
 
     const int lane = threadIdx.x;
     const int half = lane >> 5, l32 = lane & 31;
@@ -304,14 +422,6 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(NaAttnParams p) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) qf[s] = qvalid ? qrow[2 * s + half] : 0.f;
     }
-    int32_t qlo[3] = {0, 0, 0}, qhi[3] = {0, 0, 0};
-    if (p.qbox && qvalid) {
-        const int32_t* bx = p.qbox + (int64_t)qpos * 8;
-        for (int i = 0; i < 3; ++i) {
-            qlo[i] = bx[i];
-            qhi[i] = bx[3 + i];
-        }
-    }
     const float* kbase = (const float*)p.k + b * p.k_sb + h * p.k_sh;
     const float* vbase = (const float*)p.v + b * p.v_sb + h * p.v_sh;
 
@@ -324,9 +434,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(NaAttnParams p) {
 
     const int e0 = p.row_ptr[qt], e1 = p.row_ptr[qt + 1];
     for (int e = e0; e < e1; ++e) {
-        const uint32_t entry = p.entries[e];
-        const int kt = (int)(entry & ~NA_ENTRY_PARTIAL);
-        const bool partial = (entry & NA_ENTRY_PARTIAL) != 0;
+        const NaEntry entry = p.entries[e];
+        const int kt = entry.kt;
         // stage the tile: lane handles key rows lane%32, half of the columns each
         for (int row = 0; row < KV; ++row) {
             const int kp = kt * KV + row;
@@ -336,10 +445,9 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(NaAttnParams p) {
                 v_lds[row * ROW + c] = tok >= 0 ? vbase[(int64_t)tok * p.v_sn + c] : 0.f;
             }
         }
-        if (partial && lane < KV) {
-            const int kp = kt * KV + lane;
-            kc_lds[lane] = kp < N ? *(const int4*)(p.kcoord + (int64_t)kp * 4) : int4{0, 0, 0, 0};
-        }
+        // this lane's mask row (bit k = key k of the tile attended)
+        const uint32_t mk = entry.mask >= 0 ? p.masks[(int64_t)entry.mask * 32 + l32] >> (4 * half)
+                                            : 0u;
         __syncthreads();
 
         f32x16 s;
@@ -349,17 +457,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(NaAttnParams p) {
         for (int ks = 0; ks < KS; ++ks)
             s = __builtin_amdgcn_mfma_f32_32x32x2f32(k_lds[l32 * ROW + 2 * ks + half], qf[ks], s, 0,
                                                      0, 0);
-        const bool ragged = kt * KV + KV > N;
         float mt = kNegInf;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float x = s[r] * p.scale_log2;
-            if (partial || ragged) {
-                const int key = 8 * (r / 4) + 4 * half + (r % 4);
-                bool ok = kt * KV + key < N;
-                if (partial && ok) ok = in_window(qlo, qhi, kc_lds[key], p);
-                x = ok ? x : kNegInf;
-            }
+            if (entry.mask >= 0) x = keep_if(mk, 8 * (r / 4) + (r % 4), x);
             s[r] = x;
             mt = fmaxf(mt, x);
         }

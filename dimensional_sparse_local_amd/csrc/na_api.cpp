@@ -42,14 +42,14 @@ void free_device(na_plan_s* p) {
     (void)hipFree(p->d_perm);
     (void)hipFree(p->d_row_ptr);
     (void)hipFree(p->d_entries);
-    (void)hipFree(p->d_kcoord);
-    (void)hipFree(p->d_qbox);
+    (void)hipFree(p->d_masks);
+    (void)hipFree(p->d_zero);
     if (cur != p->device && cur >= 0) (void)hipSetDevice(cur);
     p->d_perm = nullptr;
     p->d_row_ptr = nullptr;
     p->d_entries = nullptr;
-    p->d_kcoord = nullptr;
-    p->d_qbox = nullptr;
+    p->d_masks = nullptr;
+    p->d_zero = nullptr;
     p->on_device = false;
 }
 
@@ -146,9 +146,11 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
         st = upload(p->identity_order ? none : p->perm, &p->d_perm);
         if (st == NA_OK) st = upload(p->row_ptr, &p->d_row_ptr);
         if (st == NA_OK) st = upload(p->entries, &p->d_entries);
-        if (st == NA_OK && p->has_partial) st = upload(p->kcoord, &p->d_kcoord);
-        if (st == NA_OK && p->has_partial) st = upload(p->qbox, &p->d_qbox);
-        if (st == NA_OK && !p->identity_order && !p->d_perm) st = NA_ERR_DEVICE;
+        if (st == NA_OK) st = upload(p->masks, &p->d_masks);
+        if (st == NA_OK) {
+            const std::vector<uint8_t> zeros(1024, 0);
+            st = upload(zeros, (uint8_t**)&p->d_zero);
+        }
         if (st != NA_OK) {
             free_device(p);
             delete p;
@@ -187,10 +189,8 @@ na_status na_plan_get_classes(na_plan_t p, uint8_t* host, size_t n) {
     }
     std::memset(host, 0, (size_t)(nq * nk));
     for (int64_t qt = 0; qt < nq; ++qt)
-        for (int32_t e = p->row_ptr[qt]; e < p->row_ptr[qt + 1]; ++e) {
-            const uint32_t ent = p->entries[e];
-            host[qt * nk + (ent & ~NA_ENTRY_PARTIAL)] = (ent & NA_ENTRY_PARTIAL) ? 1 : 2;
-        }
+        for (int32_t e = p->row_ptr[qt]; e < p->row_ptr[qt + 1]; ++e)
+            host[qt * nk + p->entries[e].kt] = p->entry_cls[e];
     return NA_OK;
 }
 
@@ -249,8 +249,8 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         na_set_error("lse must be 4-byte aligned");
         return NA_ERR_INVALID_ARG;
     }
-    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) {
-        na_set_error("scale must be finite");
+    if (!(scale > 0.f) || scale == __builtin_inff()) {
+        na_set_error("scale must be finite and positive");
         return NA_ERR_INVALID_ARG;
     }
     const na_plan_desc& d = p->desc;
@@ -282,13 +282,8 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
     a.scale_log2 = scale * 1.4426950408889634f;
     a.row_ptr = p->d_row_ptr;
     a.entries = p->d_entries;
-    a.kcoord = p->d_kcoord;
-    a.qbox = p->d_qbox;
-    a.pdims = p->pdims;
-    a.has_dilation = p->has_dilation ? 1 : 0;
-    a.dil0 = d.dilation[0];
-    a.dil1 = d.dilation[1];
-    a.dil2 = d.dilation[2];
+    a.masks = p->d_masks;
+    a.zero = p->d_zero;
     a.lse = lse;
     const int64_t N = p->n_tokens, D = d.head_dim, eb = elem_bytes(p);
 

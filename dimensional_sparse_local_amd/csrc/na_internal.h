@@ -13,9 +13,13 @@ constexpr int NA_KV_BLOCK_BF16 = 64;
 constexpr int NA_KV_BLOCK_F32 = 32;
 constexpr int NA_Q_BLOCK_F32 = 32;
 
-// A CSR entry packs the key/value tile index with a "needs per-element mask"
-// flag in the sign bit.
-constexpr uint32_t NA_ENTRY_PARTIAL = 0x80000000u;
+// One non-empty (query tile, key/value tile) pair of a CSR row: the key/value
+// tile and the index of the bit mask to apply, or -1 when every (valid query,
+// key) pair of the two tiles is attended and no key lies past the last token.
+struct NaEntry {
+    int32_t kt;
+    int32_t mask;
+};
 
 struct na_plan_s {
     na_plan_desc desc;        // normalised copy (defaults filled in)
@@ -28,20 +32,25 @@ struct na_plan_s {
     bool has_dilation = false;
     std::vector<int32_t> perm;      // sequence position -> row-major token
     std::vector<int32_t> row_ptr;   // n_q_tiles + 1
-    std::vector<uint32_t> entries;  // key/value tile | NA_ENTRY_PARTIAL
+    std::vector<NaEntry> entries;   // CSR column: non-empty key/value tiles
+    std::vector<uint8_t> entry_cls; // 1 partial, 2 full (per entry)
     std::vector<int32_t> kcoord;    // [N][4]: pattern coordinates of each position
     std::vector<int32_t> qbox;      // [N][8]: lo[3], hi[3] of each position's window
+    // Deduplicated tile masks: mask m, query row r of its tile, word w holds
+    // keys 32w .. 32w+31 of the key/value tile (bit set = attended).
+    int32_t mask_words = 0;         // ceil(kv_block / 32)
+    std::vector<uint32_t> masks;    // [n_masks][q_block][mask_words]
+    int64_t n_masks = 0;
     na_plan_stats stats{};
-    bool has_partial = false;
 
     // device copies (null when host-only or not needed)
     bool on_device = false;
     int device = -1;
     int32_t* d_perm = nullptr;
     int32_t* d_row_ptr = nullptr;
-    uint32_t* d_entries = nullptr;
-    int32_t* d_kcoord = nullptr;
-    int32_t* d_qbox = nullptr;
+    NaEntry* d_entries = nullptr;
+    uint32_t* d_masks = nullptr;
+    void* d_zero = nullptr;   // 1 KiB of zeros
 };
 
 // Thread-local error detail.
@@ -68,12 +77,9 @@ struct NaAttnParams {
     float scale_log2;      // scale * log2(e)
     const int32_t* perm;   // null = identity addressing
     const int32_t* row_ptr;
-    const uint32_t* entries;
-    const int32_t* kcoord;
-    const int32_t* qbox;
-    int32_t pdims;
-    int32_t has_dilation;
-    int32_t dil0, dil1, dil2;
+    const NaEntry* entries;
+    const uint32_t* masks;  // [n_masks][q_block][mask_words]
+    const void* zero;       // >= 1 KiB of zeros: the source of rows past the last token
 };
 
 // Returns false if no variant exists for (dtype, head_dim, q_block, kv_block).

@@ -12,6 +12,8 @@
 #include <algorithm>
 #include <cstring>
 #include <limits>
+#include <string>
+#include <unordered_map>
 
 #include "na_internal.h"
 
@@ -336,17 +338,55 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
                 if (!hit) continue;
                 cls = miss ? 1 : 2;
             }
-            if (cls == 1) {
+            if (cls == 1)
                 ++n_partial;
-                p->entries.push_back((uint32_t)kt | NA_ENTRY_PARTIAL);
-            } else {
+            else
                 ++n_full;
-                p->entries.push_back((uint32_t)kt);
-            }
+            p->entries.push_back(NaEntry{(int32_t)kt, -1});
+            p->entry_cls.push_back((uint8_t)cls);
         }
         p->row_ptr[qt + 1] = (int32_t)p->entries.size();
     }
-    p->has_partial = n_partial > 0;
+
+    // ---- element masks of partial tiles and of tiles past the last key ------
+    // Bit (row r, key k) of a tile mask: query position q0 + r and key position
+    // k0 + k are both valid tokens and the key lies in the query's window.
+    // Identical masks are stored once.
+    const int kvw = (int)ceil_div(kb, 32);
+    p->mask_words = kvw;
+    p->masks.clear();
+    std::unordered_map<std::string, int32_t> seen;
+    std::vector<uint32_t> m((size_t)(qb * kvw));
+    for (int64_t qt = 0; qt < nqt; ++qt) {
+        for (int32_t e = p->row_ptr[qt]; e < p->row_ptr[qt + 1]; ++e) {
+            const int64_t kt = p->entries[e].kt;
+            const bool full = p->entry_cls[e] == 2;
+            if (full && (kt + 1) * kb <= N) continue;  // no mask needed
+            std::fill(m.begin(), m.end(), 0u);
+            for (int64_t r = 0; r < qb; ++r) {
+                const int64_t qp = qt * qb + r;
+                if (qp >= N) break;
+                for (int64_t k = 0; k < kb; ++k) {
+                    const int64_t kp = kt * kb + k;
+                    if (kp >= N) break;
+                    if (full || inside(&p->qbox[qp * 8], &p->kcoord[kp * 4], p->pdims, dil))
+                        m[r * kvw + k / 32] |= 1u << (k % 32);
+                }
+            }
+            std::string key((const char*)m.data(), m.size() * sizeof(uint32_t));
+            auto it = seen.find(key);
+            int32_t id;
+            if (it == seen.end()) {
+                id = (int32_t)seen.size();
+                seen.emplace(std::move(key), id);
+                p->masks.insert(p->masks.end(), m.begin(), m.end());
+            } else {
+                id = it->second;
+            }
+            p->entries[e].mask = id;
+        }
+    }
+    p->n_masks = (int64_t)seen.size();
     p->stats.n_tokens = N;
     p->stats.q_block = qb;
     p->stats.kv_block = kb;

@@ -162,7 +162,8 @@ na_status na_plan_get_order(na_plan_t plan, int32_t* host_perm, size_t n);
 size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t flags);
 
 /* out = softmax attention of q over its neighbourhood keys/values, lse as
- * above.  q, k, v, out share the plan's dtype and head_dim; lse may be NULL.
+ * above.  q, k, v, out share the plan's dtype and head_dim; lse may be NULL;
+ * scale must be finite and positive (NA_ERR_INVALID_ARG otherwise).
  * Returns NA_ERR_PLAN_MISMATCH if the plan was built host-only, and
  * NA_ERR_UNSUPPORTED if no kernel matches (dtype, head_dim, q_block,
  * kv_block): bf16 with head_dim 64 or 128 and (q_block, kv_block) =
