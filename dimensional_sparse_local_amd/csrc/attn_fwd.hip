@@ -224,10 +224,11 @@ void attn_fwd_bf16(NaAttnParams p) {
             if (blk < NI) {  // wave-uniform
                 const bool real = dma_ch[i] < CS - 1 && entry.kt * KV + dma_row[i] < N;
                 const int ch = dma_ch[i] < CS - 1 ? dma_ch[i] : 0;
-                const uint16_t* gk = real ? kbase + (int64_t)tok[i] * p.k_sn + 8 * ch
-                                          : (const uint16_t*)p.zero;
-                const uint16_t* gv = real ? vbase + (int64_t)tok[i] * p.v_sn + 8 * ch
-                                          : (const uint16_t*)p.zero;
+                // offsets inside one (batch, head) slice fit in 32 bits (checked on the host)
+                const uint32_t ko = (uint32_t)tok[i] * (uint32_t)p.k_sn + 8u * ch;
+                const uint32_t vo = (uint32_t)tok[i] * (uint32_t)p.v_sn + 8u * ch;
+                const uint16_t* gk = real ? kbase + ko : (const uint16_t*)p.zero;
+                const uint16_t* gv = real ? vbase + vo : (const uint16_t*)p.zero;
                 dma16(gk, kl + blk * 512);
                 dma16(gv, vl + blk * 512);
             }
@@ -248,20 +249,26 @@ void attn_fwd_bf16(NaAttnParams p) {
     float m_ref = kNegInf;   // reference maximum (log2 domain) of O and l
     float l_run = 0.f;
 
-    // V^T transpose-read addressing: in 16-lane group g = lane/16 the source
-    // lane s = lane%16 supplies slot s/4 of its group: row 16*ks + 4*half +
-    // {0, 2, 8, 10}[s/4] (first read) or that + 1 (second read), element column
+    // Key order inside a 32-key block.  MFMA row m of S^T = K Q^T is fed by
+    // key kappa(m) = 16*(m/16) + 2*(m/8 % 2) + (m/4 % 2) + 4*(m % 4), so that
+    // the accumulator elements r of half-wave h hold keys
+    //     16*(r/8) + 2*(r/4 % 2) + h + 4*(r % 4)
+    // and each group of 4 consecutive elements holds 4 keys spaced 4 apart:
+    // rows whose 64-byte segments fall on disjoint LDS banks at the padded
+    // stride, for both the K reads and the V^T transpose reads.
+    const int kappa = 16 * (l32 >> 4) + 2 * ((l32 >> 3) & 1) + ((l32 >> 2) & 1) + 4 * (l32 & 3);
+    // V^T transpose reads: in 16-lane group g = lane/16 the source lane
+    // s = lane%16 supplies slot s/4: row 16*ks + half + 4*(s/4) (first read,
+    // elements r0..r0+3) or + 2 (second read, r0+4..r0+7), element column
     // 32*db + 16*(g%2) + 4*(s%4).
-    const int tr_slot = (lane & 15) >> 2;
-    const int tr_base = (4 * half + 2 * (tr_slot & 1) + 8 * (tr_slot >> 1)) * ROW +
-                        16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int tr_base = (half + 4 * ((lane & 15) >> 2)) * ROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     auto compute = [&](NaEntry entry, u32x2 mk, const uint16_t* kl, const uint16_t* vl) {
         // S^T = K Q^T for the two 32-key halves of the tile.
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const uint16_t* kr = kl + (32 * kb + l32) * ROW + 8 * half;
+            const uint16_t* kr = kl + (32 * kb + kappa) * ROW + 8 * half;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
@@ -271,13 +278,14 @@ void attn_fwd_bf16(NaAttnParams p) {
             }
         }
         // element mask (partial tiles and tiles past the last key only): score
-        // (kb, r) is key 32*kb + 8*(r/4) + 4*half + r%4 of the tile
+        // (kb, r) is key 32*kb + 16*(r/8) + 2*(r/4 % 2) + half + 4*(r % 4)
         if (entry.mask >= 0) {
-            const uint32_t w0 = mk[0] >> (4 * half), w1 = mk[1] >> (4 * half);
+            const uint32_t w0 = mk[0] >> half, w1 = mk[1] >> half;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                s[0][r] = keep_if(w0, 8 * (r / 4) + (r % 4), s[0][r]);
-                s[1][r] = keep_if(w1, 8 * (r / 4) + (r % 4), s[1][r]);
+                const int bit = 16 * (r / 8) + 2 * ((r / 4) % 2) + 4 * (r % 4);
+                s[0][r] = keep_if(w0, bit, s[0][r]);
+                s[1][r] = keep_if(w1, bit, s[1][r]);
             }
         }
         float mx = kNegInf;
@@ -309,21 +317,20 @@ void attn_fwd_bf16(NaAttnParams p) {
                 l_run += pe;
             }
         // O^T += V^T P^T, 16 keys per step.  Step ks covers accumulator
-        // elements r0 = 8*(ks%2) .. r0+7 of score block ks/2 (tile rows
-        // 16*ks + 4*half + {0..3, 8..11}); P^T slots take them in the order
-        // r0 + {0, 2, 4, 6, 1, 3, 5, 7}, matching the rows of the two
-        // transpose reads.
+        // elements r0 = 8*(ks%2) .. r0+7 of score block ks/2: slot e of half h
+        // is key 16*ks + 2*(e/4) + h + 4*(e%4), the row the transpose reads
+        // deliver for that slot.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const f32x16& sv = s[ks / 2];
             const int r0 = 8 * (ks % 2);
-            const bf16x8 bp = cvt8(sv[r0], sv[r0 + 2], sv[r0 + 4], sv[r0 + 6], sv[r0 + 1],
-                                   sv[r0 + 3], sv[r0 + 5], sv[r0 + 7]);
+            const bf16x8 bp = cvt8(sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
+                                   sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]);
             const uint16_t* vr = vl + tr_base + 16 * ks * ROW;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const bf16x4 lo = lds_read_tr(vr + 32 * db);
-                const bf16x4 hi = lds_read_tr(vr + ROW + 32 * db);
+                const bf16x4 hi = lds_read_tr(vr + 2 * ROW + 32 * db);
                 const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[db], 0, 0, 0);
             }

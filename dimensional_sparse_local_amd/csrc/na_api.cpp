@@ -78,6 +78,11 @@ na_status check_tensor(const na_plan_s* p, const na_tensor* t, const char* name,
     }
     (void)B;
     (void)H;
+    // element offsets inside one (batch, head) slice must fit in 31 bits
+    if ((p->n_tokens - 1) * t->stride_n + D > 0x7fffffff) {
+        na_set_error("%s: a (batch, head) slice spans more than 2^31 elements", name);
+        return NA_ERR_UNSUPPORTED;
+    }
     return NA_OK;
 }
 
