@@ -29,6 +29,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -121,6 +122,15 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// acc + sum of the 8 bf16 values of v (exact products with 1, fp32 sums).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+
 // Combine a value across the two half-waves (lanes l and l ^ 32).  The swap
 // returns {this lane's vdst, this lane's vsrc}; the partner's value sits in
 // the first for lanes 0-31 and in the second for lanes 32-63, and the other
@@ -167,7 +177,8 @@ void attn_fwd_bf16(NaAttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     const int half = lane >> 5, l32 = lane & 31;
 
     const int wg = xcd_remap(blockIdx.x, p.n_wg);
@@ -207,30 +218,46 @@ void attn_fwd_bf16(NaAttnParams p) {
         dma_row[i] = slot / CS;
         dma_ch[i] = slot % CS;
     }
+    // Pad slots copy chunk 0 of their row (never read back), so every slot of a
+    // tile that ends before the last token has a real source address.
+    int dma_off[IPW];   // element offset of this lane's chunk inside its row
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) dma_off[i] = dma_ch[i] < CS - 1 ? 8 * dma_ch[i] : 0;
     // Token of the row this lane moves in each of its DMA blocks, fetched one
-    // step ahead.  The order lookup is unconditional (clamped index) and its
-    // value is not used before the DMA is issued, so fetching it never waits.
+    // step ahead (clamped to a valid token).  Its value is not used before the
+    // DMA is issued, so fetching it never waits.
     auto tokens = [&](NaEntry entry, int* tok) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int kp = entry.kt * KV + dma_row[i];
-            tok[i] = p.perm ? gload(p.perm + (kp < N ? kp : N - 1)) : kp;
+            const int kp = min(entry.kt * KV + dma_row[i], N - 1);
+            tok[i] = p.perm ? gload(p.perm + kp) : kp;
         }
     };
     auto issue = [&](NaEntry entry, const int* tok, uint16_t* kl, uint16_t* vl) {
+        // offsets inside one (batch, head) slice fit in 32 bits (checked on the host)
+        if (entry.kt * KV + KV <= N) {
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int blk = wave + NW * i;
-            if (blk < NI) {  // wave-uniform
-                const bool real = dma_ch[i] < CS - 1 && entry.kt * KV + dma_row[i] < N;
-                const int ch = dma_ch[i] < CS - 1 ? dma_ch[i] : 0;
-                // offsets inside one (batch, head) slice fit in 32 bits (checked on the host)
-                const uint32_t ko = (uint32_t)tok[i] * (uint32_t)p.k_sn + 8u * ch;
-                const uint32_t vo = (uint32_t)tok[i] * (uint32_t)p.v_sn + 8u * ch;
-                const uint16_t* gk = real ? kbase + ko : (const uint16_t*)p.zero;
-                const uint16_t* gv = real ? vbase + vo : (const uint16_t*)p.zero;
-                dma16(gk, kl + blk * 512);
-                dma16(gv, vl + blk * 512);
+            for (int i = 0; i < IPW; ++i) {
+                const int blk = wave + NW * i;
+                if (blk < NI) {  // wave-uniform
+                    dma16(kbase + ((uint32_t)tok[i] * (uint32_t)p.k_sn + dma_off[i]), kl + blk * 512);
+                    dma16(vbase + ((uint32_t)tok[i] * (uint32_t)p.v_sn + dma_off[i]), vl + blk * 512);
+                }
+            }
+        } else {
+            // the last tile: rows past the last token come from the zero page
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int blk = wave + NW * i;
+                if (blk < NI) {
+                    const bool real = entry.kt * KV + dma_row[i] < N;
+                    const uint16_t* gk = real ? kbase + ((uint32_t)tok[i] * (uint32_t)p.k_sn + dma_off[i])
+                                              : (const uint16_t*)p.zero;
+                    const uint16_t* gv = real ? vbase + ((uint32_t)tok[i] * (uint32_t)p.v_sn + dma_off[i])
+                                              : (const uint16_t*)p.zero;
+                    dma16(gk, kl + blk * 512);
+                    dma16(gv, vl + blk * 512);
+                }
             }
         }
     };
@@ -264,18 +291,34 @@ void attn_fwd_bf16(NaAttnParams p) {
     const int tr_base = (half + 4 * ((lane & 15) >> 2)) * ROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     auto compute = [&](NaEntry entry, u32x2 mk, const uint16_t* kl, const uint16_t* vl) {
-        // S^T = K Q^T for the two 32-key halves of the tile.
+        // S^T = K Q^T for the two 32-key halves of the tile.  All KS fragments
+        // of the first half are requested up front; each MFMA of the first
+        // half is then followed by the request for the matching fragment of
+        // the second half, so LDS latency hides behind MFMA work.
         f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const uint16_t* kr = kl + (32 * kb + kappa) * ROW + 8 * half;
+        for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.f;
+        {
+            const uint16_t* kr0 = kl + kappa * ROW + 8 * half;
+            const uint16_t* kr1 = kr0 + 32 * ROW;
+            bf16x8 kf[KS];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const bf16x8*)(kr0 + 16 * ks);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *(const bf16x8*)(kr + 16 * ks);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s[0], 0, 0, 0);
+                kf[ks] = *(const bf16x8*)(kr1 + 16 * ks);
             }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s[1], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);   // KS LDS reads
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);   // KS MFMAs
         }
         // element mask (partial tiles and tiles past the last key only): score
         // (kb, r) is key 32*kb + 16*(r/8) + 2*(r/4 % 2) + half + 4*(r % 4)
@@ -311,11 +354,7 @@ void attn_fwd_bf16(NaAttnParams p) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pe = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
-                s[kb][r] = pe;
-                l_run += pe;
-            }
+            for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
         // O^T += V^T P^T, 16 keys per step.  Step ks covers accumulator
         // elements r0 = 8*(ks%2) .. r0+7 of score block ks/2: slot e of half h
         // is key 16*ks + 2*(e/4) + h + 4*(e%4), the row the transpose reads
@@ -326,6 +365,8 @@ void attn_fwd_bf16(NaAttnParams p) {
             const int r0 = 8 * (ks % 2);
             const bf16x8 bp = cvt8(sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
                                    sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]);
+            // the row sum takes the same bf16-rounded P that enters P V
+            l_run = sum_bf16x8(bp, l_run);
             const uint16_t* vr = vl + tr_base + 16 * ks * ROW;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -397,6 +438,296 @@ void attn_fwd_bf16(NaAttnParams p) {
     if (p.lse && half == 0) {
         const float lse = l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
         p.lse[(int64_t)bh * N + qtok] = lse;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, 4 waves of 48 queries each (query tile 192), key/value tile 64, built
+// on 16x16x32 MFMAs.  Each wave holds three 16-query blocks, so every K and V
+// fragment read from LDS feeds three MFMAs: a third less LDS traffic per flop
+// than 32 queries per wave, at the same two waves per SIMD.
+//
+// 16x16x32 layouts: A operand lane l holds row l%16 and reduction slots
+// 8*(l/16) .. +7; B likewise for column l%16; the accumulator lane l holds
+// column l%16 and rows 4*(l/16) .. +3.  Within a 16-key block, MFMA row m is
+// fed by key pi(m) = 4*(m%4) + 2*(m/4 % 2) + m/8, so lane-group g holds keys
+// 4*i + cg with cg = 2*(g%2) + g/2: the rows of each V^T transpose read are
+// spaced two apart (conflict-free at the padded stride) and the K reads of a
+// 16-lane phase cover 16 distinct rows.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float quad_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    const float y = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    return halves_max(y);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return halves_sum(__builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_m16(NaAttnParams p) {
+    constexpr int NW = 4;
+    constexpr int QBN = 3;                       // 16-query blocks per wave
+    constexpr int QB = 16 * QBN * NW;            // 192
+    constexpr int KV = NA_KV_BLOCK_BF16;
+    constexpr int ROW = D + 8;
+    constexpr int CS = D / 8 + 1;
+    constexpr int TILE = KV * ROW;
+    constexpr int NI = CS;
+    constexpr int IPW = (NI + NW - 1) / NW;
+    constexpr int KS = D / 32;                   // QK reduction steps
+    constexpr int DB = D / 16;                   // PV output blocks
+
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
+    // mask rows of the tile (two 32-key words per query row), DMA'd with K and V
+    __shared__ __attribute__((aligned(1024))) u32x2 m_lds0[QB];
+    __shared__ __attribute__((aligned(1024))) u32x2 m_lds1[QB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q16 = lane & 15, g = lane >> 4;
+    const int cg = 2 * (g & 1) + (g >> 1);
+
+    const int wg = xcd_remap(blockIdx.x, p.n_wg);
+    const int qt = wg % p.n_q_tiles;
+    const int bh = wg / p.n_q_tiles;
+    const int b = bh / p.heads, h = bh % p.heads;
+    const int N = p.n_tokens;
+    const float c = p.scale_log2;
+
+    // ---- this lane's three queries --------------------------------------------
+    bf16x8 qf[QBN][KS];
+#pragma unroll
+    for (int qb = 0; qb < QBN; ++qb) {
+        const int qpos = qt * QB + wave * (16 * QBN) + 16 * qb + q16;
+        const bool qvalid = qpos < N;
+        const int qtok = qvalid ? (p.perm ? p.perm[qpos] : qpos) : 0;
+        const uint16_t* qrow =
+            (const uint16_t*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qtok * p.q_sn;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (qvalid) w = *(const u32x4*)(qrow + 32 * ks + 8 * g);
+            qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+    const uint16_t* kbase = (const uint16_t*)p.k + b * p.k_sb + h * p.k_sh;
+    const uint16_t* vbase = (const uint16_t*)p.v + b * p.v_sb + h * p.v_sh;
+
+    // ---- DMA of one key/value tile (as in the 32-query kernel) -----------------
+    // slot -> (row, element offset of the chunk); recomputed where used to save
+    // registers (CS is a compile-time constant)
+    auto dma_row = [&](int i) { return (64 * (wave + NW * i) + lane) / CS; };
+    auto dma_off = [&](int i) {
+        const int ch = (64 * (wave + NW * i) + lane) % CS;
+        return ch < CS - 1 ? 8 * ch : 0;
+    };
+    auto tokens = [&](NaEntry entry, int* tok) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int kp = min(entry.kt * KV + dma_row(i), N - 1);
+            tok[i] = p.perm ? gload(p.perm + kp) : kp;
+        }
+    };
+    auto issue = [&](NaEntry entry, const int* tok, uint16_t* kl, uint16_t* vl, u32x2* ml) {
+        // the tile's mask rows: QB rows of 8 bytes = 1.5 KB, two DMA blocks
+        if (entry.mask >= 0 && wave < (QB * 8) / 1024 + 1) {
+            const int row = 128 * wave + lane * 2;   // two 8-byte rows per lane
+            if (row < QB)
+                dma16(p.masks + ((int64_t)entry.mask * QB + row) * 2, ml + 128 * wave);
+        }
+        if (entry.kt * KV + KV <= N) {
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int blk = wave + NW * i;
+                if (blk < NI) {
+                    dma16(kbase + ((uint32_t)tok[i] * (uint32_t)p.k_sn + dma_off(i)), kl + blk * 512);
+                    dma16(vbase + ((uint32_t)tok[i] * (uint32_t)p.v_sn + dma_off(i)), vl + blk * 512);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int blk = wave + NW * i;
+                if (blk < NI) {
+                    const bool real = entry.kt * KV + dma_row(i) < N;
+                    const uint16_t* gk = real ? kbase + ((uint32_t)tok[i] * (uint32_t)p.k_sn + dma_off(i))
+                                              : (const uint16_t*)p.zero;
+                    const uint16_t* gv = real ? vbase + ((uint32_t)tok[i] * (uint32_t)p.v_sn + dma_off(i))
+                                              : (const uint16_t*)p.zero;
+                    dma16(gk, kl + blk * 512);
+                    dma16(gv, vl + blk * 512);
+                }
+            }
+        }
+    };
+    f32x4 o[DB][QBN];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < QBN; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref[QBN], l_run[QBN];
+#pragma unroll
+    for (int qb = 0; qb < QBN; ++qb) {
+        m_ref[qb] = kNegInf;
+        l_run[qb] = 0.f;
+    }
+
+    const int pim = q16;   // A-operand row of this lane inside a 16-key block
+    const int pi = 4 * (pim & 3) + 2 * ((pim >> 2) & 1) + (pim >> 3);
+    const int tr_base = (4 * (q16 >> 2) + cg) * ROW + 4 * (q16 & 3);
+
+    auto compute = [&](NaEntry entry, const u32x2* ml, const uint16_t* kl, const uint16_t* vl) {
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {   // two 32-key halves of the tile
+            // S^T blocks: keys 32*hs + 16*kb .. +15, queries of block qb
+            f32x4 s[2][QBN];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QBN; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            {
+                // k-step outer, one step of lookahead: fragments of both 16-key
+                // blocks for step ks+1 load while the 6 MFMAs of step ks run
+                const uint16_t* kr = kl + (32 * hs + pi) * ROW + 8 * g;
+                bf16x8 a0 = *(const bf16x8*)(kr);
+                bf16x8 a1 = *(const bf16x8*)(kr + 16 * ROW);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    bf16x8 n0 = a0, n1 = a1;
+                    if (ks + 1 < KS) {
+                        n0 = *(const bf16x8*)(kr + 32 * (ks + 1));
+                        n1 = *(const bf16x8*)(kr + 16 * ROW + 32 * (ks + 1));
+                    }
+#pragma unroll
+                    for (int qb = 0; qb < QBN; ++qb) {
+                        s[0][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[qb][ks], s[0][qb], 0, 0, 0);
+                        s[1][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[qb][ks], s[1][qb], 0, 0, 0);
+                    }
+                    a0 = n0;
+                    a1 = n1;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // element mask: element i of block kb is key 32*hs + 16*kb + 4*i + cg
+            if (entry.mask >= 0) {
+#pragma unroll
+                for (int qb = 0; qb < QBN; ++qb) {
+                    const uint32_t w = ml[wave * (16 * QBN) + 16 * qb + q16][hs] >> cg;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s[kb][qb][i] = keep_if(w, 16 * kb + 4 * i, s[kb][qb][i]);
+                }
+            }
+#pragma unroll
+            for (int qb = 0; qb < QBN; ++qb) {
+                float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3]));
+                mx = fmaxf(mx, fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
+                mx = quad_max(mx);
+                const float m_tile = mx * c;
+                const bool grow = m_tile > m_ref[qb] + kRescaleLog2;
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float m_new = grow ? m_tile : m_ref[qb];
+                    const float alpha = grow ? fast_exp2(m_ref[qb] - m_new) : 1.f;
+                    m_ref[qb] = m_new;
+                    l_run[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[db][qb][i] *= alpha;
+                }
+                const float neg_m = m_ref[qb] == kNegInf ? 0.f : -m_ref[qb];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[kb][qb][i] = fast_exp2(__builtin_fmaf(s[kb][qb][i], c, neg_m));
+            }
+            // P^T operands: slot j = 4*kb + i of lane-group g is key 32*hs + 16*kb + 4*i + cg
+            bf16x8 bp[QBN];
+#pragma unroll
+            for (int qb = 0; qb < QBN; ++qb) {
+                bp[qb] = cvt8(s[0][qb][0], s[0][qb][1], s[0][qb][2], s[0][qb][3], s[1][qb][0],
+                              s[1][qb][1], s[1][qb][2], s[1][qb][3]);
+                l_run[qb] = sum_bf16x8(bp[qb], l_run[qb]);
+            }
+            // O^T += V^T P^T: the transpose reads give slot j' of group g the
+            // row 32*hs + 4*j' + cg (first read) or + 16 (second read)
+            const uint16_t* vr = vl + tr_base + 32 * hs * ROW;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x4 lo = lds_read_tr(vr + 16 * db);
+                const bf16x4 hi = lds_read_tr(vr + 16 * ROW + 16 * db);
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int qb = 0; qb < QBN; ++qb)
+                    o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[qb], o[db][qb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- pipelined walk over the CSR row (as in the 32-query kernel) -----------
+    const int e0 = cload(p.row_ptr + qt), e1 = cload(p.row_ptr + qt + 1);
+    const NaEntry none = {0, -1};
+    NaEntry ent_a = none, ent_b = none, ent_c = none;
+    int tok_n[IPW];
+    if (e0 < e1) {
+        ent_a = load_entry(p.entries + e0);
+        if (e0 + 1 < e1) ent_b = load_entry(p.entries + e0 + 1);
+        if (e0 + 2 < e1) ent_c = load_entry(p.entries + e0 + 2);
+        int tok0[IPW];
+        tokens(ent_a, tok0);
+        issue(ent_a, tok0, k_lds0, v_lds0, m_lds0);
+        if (e0 + 1 < e1) tokens(ent_b, tok_n);
+    }
+    auto step = [&](int e, const uint16_t* kl, const uint16_t* vl, const u32x2* ml, uint16_t* kn,
+                    uint16_t* vn, u32x2* mn) {
+        wait_vmem();
+        __syncthreads();
+        if (e + 1 < e1) issue(ent_b, tok_n, kn, vn, mn);
+        if (e + 2 < e1) tokens(ent_c, tok_n);
+        const NaEntry ent_d = e + 3 < e1 ? load_entry(p.entries + e + 3) : none;
+        compute(ent_a, ml, kl, vl);
+        ent_a = ent_b;
+        ent_b = ent_c;
+        ent_c = ent_d;
+    };
+    for (int e = e0; e < e1; e += 2) {
+        step(e, k_lds0, v_lds0, m_lds0, k_lds1, v_lds1, m_lds1);
+        if (e + 1 < e1) step(e + 1, k_lds1, v_lds1, m_lds1, k_lds0, v_lds0, m_lds0);
+    }
+
+    // ---- epilogue -----------------------------------------------------------------
+#pragma unroll
+    for (int qb = 0; qb < QBN; ++qb) {
+        const float l_tot = quad_sum(l_run[qb]);
+        const int qpos = qt * QB + wave * (16 * QBN) + 16 * qb + q16;
+        if (qpos >= N) continue;
+        const int qtok = p.perm ? p.perm[qpos] : qpos;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* orow = (uint16_t*)p.out + b * p.o_sb + h * p.o_sh + (int64_t)qtok * p.o_sn;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const f32x2 x0 = {o[db][qb][0] * inv, o[db][qb][1] * inv};
+            const f32x2 x1 = {o[db][qb][2] * inv, o[db][qb][3] * inv};
+            const uint2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(x0, bf16x2)),
+                             __builtin_bit_cast(uint32_t, __builtin_convertvector(x1, bf16x2))};
+            *(uint2*)(orow + 16 * db + 4 * g) = w;
+        }
+        if (p.lse && g == 0) {
+            const float lse = l_tot > 0.f ? (m_ref[qb] + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+            p.lse[(int64_t)bh * N + qtok] = lse;
+        }
     }
 }
 
@@ -524,7 +855,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(NaAttnParams p) {
 bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block) {
     if (dtype == NA_BF16)
         return (head_dim == 64 || head_dim == 128) && kv_block == NA_KV_BLOCK_BF16 &&
-               (q_block == 128 || q_block == 256);
+               (q_block == 128 || q_block == 192 || q_block == 256);
     if (dtype == NA_F32)
         return (head_dim == 32 || head_dim == 64) && kv_block == NA_KV_BLOCK_F32 &&
                q_block == NA_Q_BLOCK_F32;
@@ -543,6 +874,10 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
             hipLaunchKernelGGL((attn_fwd_bf16<64, 4>), grid, dim3(256), 0, st, p);
         else if (head_dim == 64 && q_block == 256)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 8>), grid, dim3(512), 0, st, p);
+        else if (head_dim == 128 && q_block == 192)
+            hipLaunchKernelGGL((attn_fwd_bf16_m16<128>), grid, dim3(256), 0, st, p);
+        else if (head_dim == 64 && q_block == 192)
+            hipLaunchKernelGGL((attn_fwd_bf16_m16<64>), grid, dim3(256), 0, st, p);
         else
             return (int)hipErrorInvalidValue;
     } else {

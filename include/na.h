@@ -167,7 +167,9 @@ size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t
  * Returns NA_ERR_PLAN_MISMATCH if the plan was built host-only, and
  * NA_ERR_UNSUPPORTED if no kernel matches (dtype, head_dim, q_block,
  * kv_block): bf16 with head_dim 64 or 128 and (q_block, kv_block) =
- * (128, 64) or (256, 64); fp32 with head_dim 32 or 64 and (32, 32). */
+ * (128, 64), (192, 64) or (256, 64); fp32 with head_dim 32 or 64 and (32, 32).
+ * In bf16 the probabilities are rounded to bf16 before they enter both P.V and
+ * the row sum, so lse carries a relative row-sum error of at most 2^-8. */
 na_status na_forward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
                      const na_tensor* k, const na_tensor* v, const na_tensor* out, float* lse,
                      float scale, uint32_t flags, void* workspace, size_t workspace_bytes,

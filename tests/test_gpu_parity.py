@@ -1,8 +1,12 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
 Tolerances: fp32 max-abs 1e-5; bf16 max-abs 2e-2 and relative L2 5e-3 on the
-output.  LSE: 1e-5 (fp32) and 1e-3 (bf16): the scores are fp32 sums of exact
-bf16 products, so the LSE error is a few fp32 ulps of |scale * q.k|.
+output.  LSE: 1e-5 (fp32) and 4e-3 (bf16).  In bf16 the kernel rounds every
+probability to bf16 (round to nearest even, relative error at most 2^-8) before
+it enters both the P.V product and the row sum, so the output stays a properly
+normalised average of v while the row sum may differ from the exact one by a
+factor in [1 - 2^-8, 1 + 2^-8]: |lse error| <= -ln(1 - 2^-8) ~= 3.92e-3, plus a
+few fp32 ulps of |scale * q.k|.
 Small cases compare every element; the full-size workloads compare sampled
 query rows (all grid corners plus seeded random rows), launched exactly as the
 benchmark launches them.
@@ -19,7 +23,7 @@ from dimensional_sparse_local_amd import workloads as W
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=1e-3)}
+TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=4e-3)}
 
 
 def _na():
@@ -111,11 +115,18 @@ def test_small_full_compare(wl):
     _run(wl)
 
 
-@pytest.mark.parametrize("q_block", [128, 256])
+@pytest.mark.parametrize("q_block", [128, 192, 256])
 def test_query_block_variants(q_block):
     wl = W.scaled(W.CONFIGS["causal1d_bf16"], name="causal_qb", H=1, grid=[777],
                   pattern=dict(kind="band", left=200, right=0))
     _run(wl, q_block=q_block)
+
+
+@pytest.mark.parametrize("name", ["sta3d_small", "sta3d_small_d64", "hilbert_small", "causal_small",
+                                  "sa3d_ragged", "gna_stride_dil"])
+def test_small_q192(name):
+    wl = [w for w in SMALL if w["name"] == name][0]
+    _run(wl, q_block=192)
 
 
 def test_hilbert_permute_passes():
