@@ -126,7 +126,10 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
         na_set_error("head_dim must be >= 1");
         return NA_ERR_INVALID_ARG;
     }
-    if (d.q_block == 0) d.q_block = d.dtype == NA_F32 ? NA_Q_BLOCK_F32 : 128;
+    // Default query tile: at head_dim 128 each key/value tile carries twice the
+    // MFMA work per byte staged, so eight waves (256 queries) share one tile.
+    if (d.q_block == 0)
+        d.q_block = d.dtype == NA_F32 ? NA_Q_BLOCK_F32 : (d.head_dim >= 128 ? 256 : 128);
     if (d.kv_block == 0) d.kv_block = d.dtype == NA_F32 ? NA_KV_BLOCK_F32 : NA_KV_BLOCK_BF16;
     if (d.q_block < 1 || d.kv_block < 1) {
         na_set_error("q_block and kv_block must be >= 1");

@@ -113,7 +113,8 @@ typedef struct {
     int32_t dilation[3];    /* >= 1 */
     int32_t causal[3];      /* 0 / 1 */
     int32_t boundary[3];    /* NA_BOUND_* (ignored for causal dimensions) */
-    int32_t q_block;        /* query tile length in tokens, 0 = library default */
+    int32_t q_block;        /* query tile length in tokens, 0 = library default (fp32: 32;
+                               bf16: 256 at head_dim 128, else 128) */
     int32_t kv_block;       /* key/value tile length in tokens, 0 = library default */
     int32_t head_dim;       /* D */
     int32_t dtype;          /* NA_BF16 or NA_F32 */

@@ -67,12 +67,12 @@ def test_config_tile_map_sta(qb):
 
 
 def test_config_class_counts():
-    # the counts recorded for the benchmark workloads at the default blocks
+    # counts of the benchmark workloads at 128-query, 64-key tiles
     expect = {"na2d_bf16": (1606, 442, 0, 692224),
               "hilbert_band_bf16": (31500, 504, 764, 8339200),
               "causal1d_bf16": (115232, 960, 14880, 125831168)}
     for name, (e, p_, f, pairs) in expect.items():
-        st = na.Plan(W.CONFIGS[name], host_only=True).stats
+        st = na.Plan(W.CONFIGS[name], host_only=True, q_block=128, kv_block=64).stats
         assert (st["n_empty"], st["n_partial"], st["n_full"], st["attended_pairs"]) == \
             (e, p_, f, pairs), name
 
