@@ -122,11 +122,43 @@ def test_query_block_variants(q_block):
     _run(wl, q_block=q_block)
 
 
-@pytest.mark.parametrize("name", ["sta3d_small", "sta3d_small_d64", "hilbert_small", "causal_small",
-                                  "sa3d_ragged", "gna_stride_dil"])
-def test_small_q192(name):
-    wl = [w for w in SMALL if w["name"] == name][0]
-    _run(wl, q_block=192)
+SMALL_BF16 = [w for w in SMALL if w["dtype"] == "bf16"]
+
+
+@pytest.mark.parametrize("q_block", [128, 192, 256])
+@pytest.mark.parametrize("wl", SMALL_BF16, ids=[w["name"] for w in SMALL_BF16])
+def test_small_every_query_block(wl, q_block):
+    """Every bf16 kernel variant (32-query waves, 48-query waves, two-group
+    256-query tiles) on every small pattern."""
+    _run(wl, q_block=q_block)
+
+
+# head_dim 128 at 256-query tiles: rows of 2 to ~40 key tiles (both LDS
+# buffers, odd and even row lengths), ragged token counts, gathered orders
+# (tiled, Hilbert), strided / dilated windows and partial tiles
+D128_QB256 = [
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="d128_tiny", H=1, grid=[70],
+             pattern=dict(kind="band", left=5, right=5)),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="d128_causal_ragged", H=2, grid=[3000],
+             pattern=dict(kind="band", left=600, right=0)),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="d128_band_even", B=2, H=1, grid=[2048],
+             pattern=dict(kind="band", left=130, right=190)),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="d128_na2d_ragged", B=1, H=2, D=128, grid=[40, 50],
+             pattern=dict(kind="na", window=[9, 11])),
+    W.scaled(W.CONFIGS["hilbert_band_bf16"], name="d128_hilbert", B=1, H=2, D=128, grid=[32, 32],
+             pattern=dict(kind="band", left=100, right=100)),
+    W.scaled(W.CONFIGS["sta3d_bf16"], name="d128_sta_wide", H=2, grid=[12, 16, 40],
+             pattern=dict(kind="sta", tile=[6, 8, 8], window_tiles=[1, 2, 3])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="d128_gna", B=1, H=1, D=128, grid=[19, 23],
+             pattern=dict(kind="na", window=[7, 5], stride=[3, 2], dilation=[2, 1])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="d128_sa3d", B=1, H=1, D=128, grid=[5, 7, 9],
+             pattern=dict(kind="sa", window=[3, 5, 3])),
+]
+
+
+@pytest.mark.parametrize("wl", D128_QB256, ids=[w["name"] for w in D128_QB256])
+def test_d128_q256(wl):
+    _run(wl, q_block=256)
 
 
 def test_hilbert_permute_passes():
