@@ -93,6 +93,11 @@ def lib():
                                     ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int32]
+        L.orc_attention_backward.argtypes = [P(_Spec), ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int32]
         L.orc_tile_classes.argtypes = [P(_Spec), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                        P(ctypes.c_int64), ctypes.c_int32]
         L.orc_max_threads.restype = ctypes.c_int32
@@ -204,17 +209,21 @@ def attended_pairs(workload: dict) -> int:
 
 def _raw(x) -> tuple[np.ndarray, int]:
     """(contiguous raw array, dtype code) for a numpy array or CPU torch tensor.
-    Code 0: bf16 bit patterns (uint16); code 1: float32."""
+    Code 0: bf16 bit patterns (uint16); 1: float32; 2: float64."""
     if hasattr(x, "detach"):  # a torch tensor
         import torch
 
         x = x.detach().cpu().contiguous()
         if x.dtype == torch.bfloat16:
             return np.ascontiguousarray(x.view(torch.int16).numpy().view(np.uint16)), 0
+        if x.dtype == torch.float64:
+            return np.ascontiguousarray(x.numpy()), 2
         return np.ascontiguousarray(x.float().numpy()), 1
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return np.ascontiguousarray(x), 0
+    if x.dtype == np.float64:
+        return np.ascontiguousarray(x), 2
     return np.ascontiguousarray(x, dtype=np.float32), 1
 
 
@@ -245,6 +254,29 @@ def attention(workload: dict, q, k, v, scale: float, rows=None, threads: int = 0
     if rc != 0:
         raise ValueError("oracle attention failed (%d)" % rc)
     return out, lse
+
+
+def attention_backward(workload: dict, q, k, v, dout, scale: float, threads: int = 0):
+    """fp64 gradients (dq, dk, dv), each [B, H, N, D], of sum(out * dout) where
+    out = attention(workload, q, k, v, scale) over all rows.  Inputs as for
+    attention(); dout of the same dtype."""
+    s = spec(workload)
+    qa, dt = _raw(q)
+    ka, dk_ = _raw(k)
+    va, dv_ = _raw(v)
+    ga, dg = _raw(dout)
+    assert dt == dk_ == dv_ == dg, "q, k, v, dout must share a dtype"
+    B, H, N, D = qa.shape
+    assert N == num_tokens(workload)
+    dq = np.empty((B, H, N, D), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    rc = lib().orc_attention_backward(ctypes.byref(s), B, H, D, dt, _ptr(qa), _ptr(ka), _ptr(va),
+                                      _ptr(ga), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      int(threads))
+    if rc != 0:
+        raise ValueError("oracle backward failed (%d)" % rc)
+    return dq, dk, dv
 
 
 def tile_classes(workload: dict, q_block: int, kv_block: int, threads: int = 0):

@@ -1,5 +1,5 @@
 /*
- * Plain fp64 CPU oracle for N-dimensional local attention (forward only).
+ * Plain fp64 CPU oracle for N-dimensional local attention (forward and its gradients).
  *
  * TEST INFRASTRUCTURE ONLY: called from the tests, the smoke check and the
  * CPU-baseline leg of the benchmark, never from the product path.  It shares
@@ -265,6 +265,7 @@ int64_t orc_attended_pairs(const orc_spec* s) {
 /* ------------------------------------------------------------------------ */
 
 static double load_elem(const void* base, int32_t dtype, int64_t idx) {
+    if (dtype == 2) return ((const double*)base)[idx];
     if (dtype == 1) return (double)((const float*)base)[idx];
     uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
     float f;
@@ -343,6 +344,97 @@ int orc_attention(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dt
     free(pos);
     free(perm);
     return err ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gradients of the restricted attention.                                   */
+/* ------------------------------------------------------------------------ */
+
+/* For every query i with a non-empty N(i), in the order of the definition:
+     z_ij = scale q_i . k_j                       (pi-Attention, Eq. 4)
+     P_ij = exp(z_ij) / sum_j' exp(z_ij')         (Eq. 2, over N(i))
+     dP_ij = dout_i . v_j                         (Eq. 3 is linear in P)
+     dz_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')   (softmax Jacobian, Eq. 23)
+     dq_i += scale dz_ij k_j,  dk_j += scale dz_ij q_i,  dv_j += P_ij dout_i.
+   Every (batch, head) slice is owned by one thread, so the scatter into dk and
+   dv needs no synchronisation. */
+int orc_attention_backward(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dtype,
+                           const void* q, const void* k, const void* v, const void* dout,
+                           double scale, double* dq, double* dk, double* dv, int32_t threads) {
+    const int64_t N = orc_num_tokens(s);
+    int64_t* perm = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (orc_order(s, perm) != 0) {
+        free(perm);
+        return -1;
+    }
+    int64_t* pos = invert(perm, N);
+    const int64_t total = B * H * N * D;
+    for (int64_t t = 0; t < total; ++t) dq[t] = dk[t] = dv[t] = 0.0;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+        double* p = (double*)malloc(sizeof(double) * (size_t)N);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+        double* qi = (double*)malloc(sizeof(double) * (size_t)D);
+        double* gi = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * H; ++bh) {
+            const int64_t head = bh * N * D;
+            for (int64_t i = 0; i < N; ++i) {
+                const int64_t n = orc_neighbors(s, perm, pos, i, nb);
+                if (n == 0) continue;   /* out_i = 0 does not depend on q, k, v */
+                for (int64_t d = 0; d < D; ++d) {
+                    qi[d] = load_elem(q, dtype, head + i * D + d);
+                    gi[d] = load_elem(dout, dtype, head + i * D + d);
+                }
+                double m = -INFINITY;
+                for (int64_t a = 0; a < n; ++a) {
+                    const int64_t kj = head + nb[a] * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += qi[d] * load_elem(k, dtype, kj + d);
+                    p[a] = scale * dot;
+                    if (p[a] > m) m = p[a];
+                }
+                double l = 0.0;
+                for (int64_t a = 0; a < n; ++a) {
+                    p[a] = exp(p[a] - m);
+                    l += p[a];
+                }
+                double delta = 0.0;
+                for (int64_t a = 0; a < n; ++a) {
+                    p[a] /= l;
+                    const int64_t vj = head + nb[a] * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += gi[d] * load_elem(v, dtype, vj + d);
+                    dp[a] = dot;
+                    delta += p[a] * dot;
+                }
+                double* dqi = dq + head + i * D;
+                for (int64_t a = 0; a < n; ++a) {
+                    const double dz = p[a] * (dp[a] - delta);
+                    const int64_t j = head + nb[a] * D;
+                    for (int64_t d = 0; d < D; ++d) {
+                        dqi[d] += scale * dz * load_elem(k, dtype, j + d);
+                        dk[j + d] += scale * dz * qi[d];
+                        dv[j + d] += p[a] * gi[d];
+                    }
+                }
+            }
+        }
+        free(gi);
+        free(qi);
+        free(dp);
+        free(p);
+        free(nb);
+    }
+    free(pos);
+    free(perm);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -1,5 +1,6 @@
 /*
- * Plain fp64 CPU oracle for N-dimensional local attention (forward only).
+ * Plain fp64 CPU oracle for N-dimensional local attention: the forward pass
+ * and its gradients.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link
  * or call this code; it exists so that tests, the smoke check and the CPU
@@ -87,7 +88,7 @@ int64_t orc_attended_pairs(const orc_spec* s);
 
 /* Softmax attention restricted to N(i).
    q, k, v: contiguous [B][H][N][D]; dtype 0 = bf16 bit patterns (uint16),
-   1 = float32.  rows: the row-major query tokens to evaluate (nrows of them),
+   1 = float32, 2 = float64.  rows: the row-major query tokens to evaluate (nrows of them),
    or NULL with nrows = N for all.  out: [B][H][nrows][D] fp64,
    lse: [B][H][nrows] fp64 (natural log of the sum of exp of scaled logits).
    threads <= 0 uses the OpenMP default.  Returns 0 on success. */
@@ -95,6 +96,14 @@ int orc_attention(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dt
                   const void* q, const void* k, const void* v, double scale,
                   const int64_t* rows, int64_t nrows, double* out, double* lse,
                   int32_t threads);
+
+/* Gradients of sum_i dout_i . out_i with respect to q, k, v, where out is the
+   attention above over all N rows.  q, k, v, dout: contiguous [B][H][N][D] of
+   one dtype (codes as above); dq, dk, dv: [B][H][N][D] fp64.  Rows with an
+   empty neighbourhood contribute nothing.  Returns 0 on success. */
+int orc_attention_backward(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dtype,
+                           const void* q, const void* k, const void* v, const void* dout,
+                           double scale, double* dq, double* dk, double* dv, int32_t threads);
 
 /* Tile classes over the sequence order: cls[qt * nkt + kt] in {0 empty,
    1 partial, 2 full}; nqt = ceil(N/q_block), nkt = ceil(N/kv_block).

@@ -1,0 +1,141 @@
+"""Pins of the oracle's gradients (dq, dk, dv of sum(out * dout)).
+
+The pages state the softmax Jacobian ("pi-Attention", gradient analysis of
+adaptive fusion, Eq. 23) but print no gradient values, so the backward oracle
+is pinned against facts that do not use its arithmetic:
+
+* central finite differences of the forward oracle in float64 on tiny grids
+  (every pattern kind, both orders with gathers, strides and dilation),
+* reverse-mode autograd of a dense masked softmax attention written with
+  library routines (torch, CPU, float64),
+* closed forms: the gradient is unchanged by adding one vector to every key of
+  a neighbourhood, so the dk of each slice sums to zero; the rows of P sum to
+  one, so the dv of each slice sums to the sum of dout; a one-token window
+  gives dv = dout and dq = dk = 0.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dimensional_sparse_local_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+TINY = [
+    dict(name="band_causal", B=1, H=1, D=3, dtype="fp32", grid=[9], order="row_major",
+         pattern=dict(kind="band", left=3, right=0)),
+    dict(name="band_two_sided", B=1, H=2, D=2, dtype="fp32", grid=[8], order="row_major",
+         pattern=dict(kind="band", left=2, right=1)),
+    dict(name="na2d", B=1, H=1, D=3, dtype="fp32", grid=[4, 5], order="row_major",
+         pattern=dict(kind="na", window=[3, 3])),
+    dict(name="sa2d", B=1, H=1, D=2, dtype="fp32", grid=[4, 4], order="row_major",
+         pattern=dict(kind="sa", window=[3, 3])),
+    dict(name="sta_tiled", B=1, H=1, D=2, dtype="fp32", grid=[4, 6], order="tiled", tile=[2, 3],
+         pattern=dict(kind="sta", tile=[2, 3], window_tiles=[1, 1])),
+    dict(name="hilbert_band", B=1, H=1, D=2, dtype="fp32", grid=[4, 4], order="hilbert",
+         pattern=dict(kind="band", left=2, right=2)),
+    dict(name="gna_stride_dil", B=1, H=1, D=2, dtype="fp32", grid=[7, 5], order="row_major",
+         pattern=dict(kind="na", window=[3, 3], stride=[2, 1], dilation=[1, 2])),
+]
+
+
+def _loss(wl, q, k, v, g, scale):
+    out, _ = oracle.attention(wl, q, k, v, scale)
+    return float(np.sum(out * g))
+
+
+@pytest.mark.parametrize("wl", TINY, ids=[w["name"] for w in TINY])
+def test_backward_finite_differences(wl):
+    B, H, D = wl["B"], wl["H"], wl["D"]
+    N = W.num_tokens(wl)
+    q, k, v, g = (_rand((B, H, N, D), s) for s in (11, 12, 13, 14))
+    scale = 0.7
+    dq, dk, dv = oracle.attention_backward(wl, q, k, v, g, scale)
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            fp = _loss(wl, q, k, v, g, scale)
+            x[idx] = keep - h
+            fm = _loss(wl, q, k, v, g, scale)
+            x[idx] = keep
+            num[idx] = (fp - fm) / (2 * h)
+        err = np.max(np.abs(num - grad))
+        assert err < 1e-7, "%s: d%s max-abs %.3e" % (wl["name"], name, err)
+
+
+def _autograd_masked(q, k, v, g, mask, scale):
+    """Dense softmax attention with a boolean [N, N] mask, reverse mode."""
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    logits = scale * torch.matmul(qt, kt.transpose(-1, -2).contiguous())
+    logits = logits.masked_fill(~torch.tensor(mask), float("-inf"))
+    out = torch.matmul(torch.softmax(logits, dim=-1), vt)
+    out.backward(torch.tensor(g, dtype=torch.float64))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+MASKED = [
+    W.scaled(W.CONFIGS["na2d_fp32"], name="dense", grid=[5, 6], D=8, H=2,
+             pattern=dict(kind="na", window=[5, 6])),
+    W.scaled(W.CONFIGS["na2d_fp32"], name="na", grid=[7, 6], D=8, H=2,
+             pattern=dict(kind="na", window=[3, 5])),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="causal", dtype="fp32", H=2, D=16, grid=[40],
+             pattern=dict(kind="band", left=9, right=0)),
+    W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert", dtype="fp32", B=1, H=1, D=8,
+             grid=[8, 8], pattern=dict(kind="band", left=5, right=3)),
+    W.scaled(W.CONFIGS["sta3d_bf16"], name="sta3d", dtype="fp32", H=1, D=8, grid=[4, 4, 6],
+             pattern=dict(kind="sta", tile=[2, 2, 3], window_tiles=[1, 2, 1])),
+]
+
+
+@pytest.mark.parametrize("wl", MASKED, ids=[w["name"] for w in MASKED])
+def test_backward_matches_masked_dense_autograd(wl):
+    B, H, D = wl["B"], wl["H"], wl["D"]
+    N = W.num_tokens(wl)
+    q, k, v, g = (_rand((B, H, N, D), s) for s in (21, 22, 23, 24))
+    mask = np.zeros((N, N), dtype=bool)
+    for i in range(N):
+        mask[i, oracle.neighbors(wl, i)] = True
+    scale = 1.0 / np.sqrt(D)
+    want = _autograd_masked(q, k, v, g, mask, scale)
+    got = oracle.attention_backward(wl, q, k, v, g, scale)
+    for name, a, b in zip("qkv", got, want):
+        assert np.max(np.abs(a - b)) < 1e-10, "%s d%s" % (wl["name"], name)
+
+
+@pytest.mark.parametrize("wl", MASKED[1:], ids=[w["name"] for w in MASKED[1:]])
+def test_backward_closed_forms(wl):
+    B, H, D = wl["B"], wl["H"], wl["D"]
+    N = W.num_tokens(wl)
+    q, k, v, g = (_rand((B, H, N, D), s) for s in (31, 32, 33, 34))
+    dq, dk, dv = oracle.attention_backward(wl, q, k, v, g, 0.3)
+    # every query attends itself, so no row is empty
+    assert np.max(np.abs(dk.sum(axis=2))) < 1e-10
+    assert np.max(np.abs(dv.sum(axis=2) - g.sum(axis=2))) < 1e-10
+
+
+def test_backward_one_token_window():
+    wl = W.scaled(W.CONFIGS["na2d_fp32"], name="one", grid=[5, 7], pattern=dict(kind="na", window=[1, 1]))
+    N = W.num_tokens(wl)
+    q, k, v, g = (_rand((1, 1, N, 32), s) for s in (41, 42, 43, 44))
+    dq, dk, dv = oracle.attention_backward(wl, q, k, v, g, 0.5)
+    assert np.array_equal(dv, g)
+    assert not dq.any() and not dk.any()
+
+
+def test_backward_bf16_inputs_are_upcast_exactly():
+    wl = W.scaled(W.CONFIGS["causal1d_bf16"], name="bf16", H=1, D=8, grid=[30],
+                  pattern=dict(kind="band", left=4, right=0))
+    N = W.num_tokens(wl)
+    xs = [torch.tensor(_rand((1, 1, N, 8), s)).to(torch.bfloat16) for s in (51, 52, 53, 54)]
+    a = oracle.attention_backward(wl, *xs, 0.25)
+    b = oracle.attention_backward(wl, *[x.double() for x in xs], 0.25)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
