@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libna.so")
 
 HOST_SOURCES = ["plan.cpp", "na_api.cpp"]
-DEVICE_SOURCES = ["attn_fwd.hip", "permute.hip"]
+DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "permute.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
@@ -24,6 +24,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 # instructions (infinities, used for masked scores, are still honoured).
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
                 "-packed-fp32-ops", "-fno-honor-nans"]
+# Per-source extras.  The key-major gradient kernel runs one wave per SIMD with
+# up to 512 registers: its MFMA accumulators stay in ordinary vector registers
+# (the softmax reads them directly) and the accumulation registers serve as
+# spill space.
+SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd, verbose):
@@ -40,7 +45,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     procs, objs = [], []
     for src in HOST_SOURCES + DEVICE_SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc] + COMMON + DEVICE_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([hipcc] + COMMON + DEVICE_FLAGS + SOURCE_FLAGS.get(src, []) +
+               ["-c", os.path.join(CSRC, src), "-o", obj])
         if src.endswith(".cpp"):
             cmd = [hipcc] + COMMON + ["-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src),
                                       "-o", obj]

@@ -1,0 +1,130 @@
+// Device helpers shared by the attention kernels (gfx950): vector types, LDS
+// transpose reads and LDS DMA, bf16 conversion, half-wave reductions and the
+// XCD-aware workgroup order.
+//
+// MFMA 32x32 accumulator layout used throughout: lane l, element r holds
+// row 8*(r/4) + 4*(l/32) + r%4 and column l%32.  A and B operands: lane l holds
+// row (A) / column (B) l%32 and reduction slots 8*(l/32)..8*(l/32)+7 (bf16) or
+// slot l/32 (fp32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "na_internal.h"
+
+namespace {
+
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Load through a global-address-space pointer (a flat load would also count
+// against the LDS wait counter).
+template <typename T>
+__device__ __forceinline__ T gload(const T* ptr) {
+    return *(const __attribute__((address_space(1))) T*)(ptr);
+}
+
+// Load of read-only, wave-uniform data through the constant address space
+// (a scalar load).
+template <typename T>
+__device__ __forceinline__ T cload(const T* ptr) {
+    return *(const __attribute__((address_space(4))) T*)(ptr);
+}
+
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ NaEntry load_entry(const NaEntry* e) {
+    const i32x2 v = cload((const i32x2*)e);
+    return NaEntry{v[0], v[1]};
+}
+
+// Keep score x when bit `bit` of word w is set, else -inf.
+__device__ __forceinline__ float keep_if(uint32_t w, int bit, float x) {
+    return (w >> bit) & 1u ? x : kNegInf;
+}
+
+// Online softmax in the log2 domain with a lazy rescale: a row's reference
+// maximum moves (and O, l are rescaled) only when the tile maximum exceeds it
+// by more than 2^8, which keeps every P <= 256 and is exact after the final
+// division by l.
+constexpr float kRescaleLog2 = 8.0f;
+
+typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)(lds), 16, 0, 0);
+}
+
+// Wait for all of this wave's vector memory operations (including LDS DMA).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                       float a6, float a7) {
+    const f32x2 x0 = {a0, a1}, x1 = {a2, a3}, x2 = {a4, a5}, x3 = {a6, a7};
+    const bf16x2 y0 = __builtin_convertvector(x0, bf16x2);
+    const bf16x2 y1 = __builtin_convertvector(x1, bf16x2);
+    const bf16x2 y2 = __builtin_convertvector(x2, bf16x2);
+    const bf16x2 y3 = __builtin_convertvector(x3, bf16x2);
+    u32x4 w = {__builtin_bit_cast(uint32_t, y0), __builtin_bit_cast(uint32_t, y1),
+               __builtin_bit_cast(uint32_t, y2), __builtin_bit_cast(uint32_t, y3)};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// acc + sum of the 8 bf16 values of v (exact products with 1, fp32 sums).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+
+// Combine a value across the two half-waves (lanes l and l ^ 32).  The swap
+// returns {this lane's vdst, this lane's vsrc}; the partner's value sits in
+// the first for lanes 0-31 and in the second for lanes 32-63, and the other
+// element holds the lane's own value, so a symmetric reduction of the pair is
+// the same on every lane.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Workgroup index -> logical tile index.  Workgroups are dispatched to the 8
+// XCDs round-robin; give each XCD one contiguous range of logical tiles
+// (consecutive query tiles of one head) so that the tiles sharing key/value
+// tiles share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    constexpr int kXcd = 8;
+    const int q = n / kXcd, r = n % kXcd;
+    const int x = bid % kXcd, local = bid / kXcd;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
+}  // namespace

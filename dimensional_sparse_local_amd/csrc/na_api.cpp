@@ -42,12 +42,16 @@ void free_device(na_plan_s* p) {
     (void)hipFree(p->d_perm);
     (void)hipFree(p->d_row_ptr);
     (void)hipFree(p->d_entries);
+    (void)hipFree(p->d_t_row_ptr);
+    (void)hipFree(p->d_t_entries);
     (void)hipFree(p->d_masks);
     (void)hipFree(p->d_zero);
     if (cur != p->device && cur >= 0) (void)hipSetDevice(cur);
     p->d_perm = nullptr;
     p->d_row_ptr = nullptr;
     p->d_entries = nullptr;
+    p->d_t_row_ptr = nullptr;
+    p->d_t_entries = nullptr;
     p->d_masks = nullptr;
     p->d_zero = nullptr;
     p->on_device = false;
@@ -151,6 +155,8 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
         st = upload(p->identity_order ? none : p->perm, &p->d_perm);
         if (st == NA_OK) st = upload(p->row_ptr, &p->d_row_ptr);
         if (st == NA_OK) st = upload(p->entries, &p->d_entries);
+        if (st == NA_OK) st = upload(p->t_row_ptr, &p->d_t_row_ptr);
+        if (st == NA_OK) st = upload(p->t_entries, &p->d_t_entries);
         if (st == NA_OK) st = upload(p->masks, &p->d_masks);
         if (st == NA_OK) {
             const std::vector<uint8_t> zeros(1024, 0);
@@ -339,6 +345,99 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
             rc = na_permute_launch(ls, lse, B, H, N, 4, H * N * 4, N * 4, 4, H * N * 4, N * 4, 4,
                                    p->d_perm, 1, stream);
     }
+    if (rc != 0) {
+        na_set_error("kernel launch failed: %s", hip_err((hipError_t)rc));
+        return NA_ERR_DEVICE;
+    }
+    return NA_OK;
+}
+
+size_t na_backward_workspace_bytes(na_plan_t p, int64_t B, int64_t H) {
+    if (!p || B < 1 || H < 1) return 0;
+    return ((size_t)B * (size_t)H * (size_t)p->n_tokens * sizeof(float) + 255) & ~(size_t)255;
+}
+
+na_status na_backward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, const na_tensor* k,
+                      const na_tensor* v, const na_tensor* out, const na_tensor* dout,
+                      const float* lse, const na_tensor* dq, const na_tensor* dk,
+                      const na_tensor* dv, float scale, void* workspace, size_t ws_bytes,
+                      void* stream) {
+    if (!p) {
+        na_set_error("plan is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (!p->on_device) {
+        na_set_error("plan was built host-only and cannot run");
+        return NA_ERR_PLAN_MISMATCH;
+    }
+    if (B < 1 || H < 1) {
+        na_set_error("B and H must be >= 1");
+        return NA_ERR_INVALID_ARG;
+    }
+    const int64_t nq = p->stats.n_q_tiles * B * H, nk = p->stats.n_kv_tiles * B * H;
+    if (nq > 0x7fffffff || nk > 0x7fffffff || B * H > 0x7fffffff / (p->n_tokens > 0 ? p->n_tokens : 1)) {
+        na_set_error("B * H * tiles too large");
+        return NA_ERR_INVALID_ARG;
+    }
+    na_status st;
+    const na_tensor* ts[8] = {q, k, v, out, dout, dq, dk, dv};
+    const char* names[8] = {"q", "k", "v", "out", "dout", "dq", "dk", "dv"};
+    for (int i = 0; i < 8; ++i)
+        if ((st = check_tensor(p, ts[i], names[i], B, H)) != NA_OK) return st;
+    if (!lse || ((uintptr_t)lse) % 4 != 0) {
+        na_set_error("lse must be a 4-byte aligned fp32 [B, H, N] array");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (!(scale > 0.f) || scale == __builtin_inff()) {
+        na_set_error("scale must be finite and positive");
+        return NA_ERR_INVALID_ARG;
+    }
+    const na_plan_desc& d = p->desc;
+    if (!na_bwd_supported(d.dtype, d.head_dim, d.q_block, d.kv_block)) {
+        na_set_error("no gradient kernels for dtype=%d head_dim=%d q_block=%d kv_block=%d",
+                     d.dtype, d.head_dim, d.q_block, d.kv_block);
+        return NA_ERR_UNSUPPORTED;
+    }
+    const size_t need = na_backward_workspace_bytes(p, B, H);
+    if (!workspace || ws_bytes < need || ((uintptr_t)workspace) % 256 != 0) {
+        na_set_error("backward needs %zu bytes of 256-byte aligned workspace", need);
+        return NA_ERR_INVALID_ARG;
+    }
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != p->device) {
+        na_set_error("plan lives on device %d, current device is %d", p->device, cur);
+        return NA_ERR_PLAN_MISMATCH;
+    }
+    NaBwdParams a{};
+    a.q = q->ptr, a.k = k->ptr, a.v = v->ptr, a.out = out->ptr, a.dout = dout->ptr;
+    a.dq = dq->ptr, a.dk = dk->ptr, a.dv = dv->ptr;
+    a.lse = lse;
+    a.delta = (float*)workspace;
+    a.q_sb = q->stride_b, a.q_sh = q->stride_h, a.q_sn = q->stride_n;
+    a.k_sb = k->stride_b, a.k_sh = k->stride_h, a.k_sn = k->stride_n;
+    a.v_sb = v->stride_b, a.v_sh = v->stride_h, a.v_sn = v->stride_n;
+    a.o_sb = out->stride_b, a.o_sh = out->stride_h, a.o_sn = out->stride_n;
+    a.g_sb = dout->stride_b, a.g_sh = dout->stride_h, a.g_sn = dout->stride_n;
+    a.dq_sb = dq->stride_b, a.dq_sh = dq->stride_h, a.dq_sn = dq->stride_n;
+    a.dk_sb = dk->stride_b, a.dk_sh = dk->stride_h, a.dk_sn = dk->stride_n;
+    a.dv_sb = dv->stride_b, a.dv_sh = dv->stride_h, a.dv_sn = dv->stride_n;
+    a.batch = (int32_t)B;
+    a.n_tokens = (int32_t)p->n_tokens;
+    a.heads = (int32_t)H;
+    a.n_q_tiles = (int32_t)p->stats.n_q_tiles;
+    a.n_kv_tiles = (int32_t)p->stats.n_kv_tiles;
+    a.q_block = (int32_t)d.q_block;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.perm = p->identity_order ? nullptr : p->d_perm;
+    a.row_ptr = p->d_row_ptr;
+    a.entries = p->d_entries;
+    a.t_row_ptr = p->d_t_row_ptr;
+    a.t_entries = p->d_t_entries;
+    a.masks = p->d_masks;
+    a.zero = p->d_zero;
+    if (p->n_tokens == 0) return NA_OK;
+    const int rc = na_bwd_launch(a, d.head_dim, stream);
     if (rc != 0) {
         na_set_error("kernel launch failed: %s", hip_err((hipError_t)rc));
         return NA_ERR_DEVICE;

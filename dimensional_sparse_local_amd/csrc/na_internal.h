@@ -41,6 +41,12 @@ struct na_plan_s {
     int32_t mask_words = 0;         // ceil(kv_block / 32)
     std::vector<uint32_t> masks;    // [n_masks][q_block][mask_words]
     int64_t n_masks = 0;
+    // The same tile map by key/value tile (for the gradients of K and V): for
+    // key/value tile kt, entries t_row_ptr[kt] .. t_row_ptr[kt+1] of t_entries
+    // hold the query tiles that attend it (field kt = query tile) in ascending
+    // order, with the mask ids of the query-major map.
+    std::vector<int32_t> t_row_ptr; // n_kv_tiles + 1
+    std::vector<NaEntry> t_entries;
     na_plan_stats stats{};
 
     // device copies (null when host-only or not needed)
@@ -50,6 +56,8 @@ struct na_plan_s {
     int32_t* d_row_ptr = nullptr;
     NaEntry* d_entries = nullptr;
     uint32_t* d_masks = nullptr;
+    int32_t* d_t_row_ptr = nullptr;
+    NaEntry* d_t_entries = nullptr;
     void* d_zero = nullptr;   // 1 KiB of zeros
 };
 
@@ -81,6 +89,49 @@ struct NaAttnParams {
     const uint32_t* masks;  // [n_masks][q_block][mask_words]
     const void* zero;       // >= 1 KiB of zeros: the source of rows past the last token
 };
+
+// Gradient launch parameters (attn_bwd.hip).  Tensors as in NaAttnParams;
+// g = dout, lse and delta are fp32 [B][H][N] in row-major token order.
+struct NaBwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    float* delta;          // workspace: dout_i . out_i
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t q_sb, q_sh, q_sn;
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t o_sb, o_sh, o_sn;
+    int64_t g_sb, g_sh, g_sn;
+    int64_t dq_sb, dq_sh, dq_sn;
+    int64_t dk_sb, dk_sh, dk_sn;
+    int64_t dv_sb, dv_sh, dv_sn;
+    int32_t batch;
+    int32_t n_tokens;
+    int32_t heads;
+    int32_t n_q_tiles;
+    int32_t n_kv_tiles;
+    int32_t q_block;
+    float scale;
+    float scale_log2;      // scale * log2(e)
+    const int32_t* perm;   // null = identity addressing
+    const int32_t* row_ptr;
+    const NaEntry* entries;
+    const int32_t* t_row_ptr;
+    const NaEntry* t_entries;
+    const uint32_t* masks;
+    const void* zero;      // >= 1 KiB of zeros
+};
+
+// Returns false if no gradient kernels exist for (dtype, head_dim, q_block, kv_block).
+bool na_bwd_supported(int dtype, int head_dim, int q_block, int kv_block);
+// Launch the three gradient kernels (row sums, dq, dk/dv); HIP error code.
+int na_bwd_launch(const NaBwdParams& p, int head_dim, void* stream);
 
 // Returns false if no variant exists for (dtype, head_dim, q_block, kv_block).
 bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block);

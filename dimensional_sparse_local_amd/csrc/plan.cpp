@@ -390,6 +390,18 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
         }
     }
     p->n_masks = (int64_t)seen.size();
+
+    // ---- the same map by key/value tile --------------------------------------
+    p->t_row_ptr.assign(nkt + 1, 0);
+    for (const NaEntry& e : p->entries) ++p->t_row_ptr[e.kt + 1];
+    for (int64_t kt = 0; kt < nkt; ++kt) p->t_row_ptr[kt + 1] += p->t_row_ptr[kt];
+    p->t_entries.assign(p->entries.size(), NaEntry{0, -1});
+    {
+        std::vector<int32_t> fill(p->t_row_ptr.begin(), p->t_row_ptr.end() - 1);
+        for (int64_t qt = 0; qt < nqt; ++qt)
+            for (int32_t e = p->row_ptr[qt]; e < p->row_ptr[qt + 1]; ++e)
+                p->t_entries[fill[p->entries[e].kt]++] = NaEntry{(int32_t)qt, p->entries[e].mask};
+    }
     p->stats.n_tokens = N;
     p->stats.q_block = qb;
     p->stats.kv_block = kb;

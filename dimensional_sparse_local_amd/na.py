@@ -80,12 +80,17 @@ def lib():
         L.na_forward.argtypes = [vp, i64, i64, P(Tensor), P(Tensor), P(Tensor), P(Tensor), vp,
                                  ctypes.c_float, u32, vp, ctypes.c_size_t, vp]
         L.na_permute.argtypes = [vp, i64, i64, P(Tensor), P(Tensor), ctypes.c_int32, vp]
+        L.na_backward_workspace_bytes.argtypes = [vp, i64, i64]
+        L.na_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.na_backward.argtypes = [vp, i64, i64, P(Tensor), P(Tensor), P(Tensor), P(Tensor),
+                                  P(Tensor), vp, P(Tensor), P(Tensor), P(Tensor), ctypes.c_float,
+                                  vp, ctypes.c_size_t, vp]
         L.na_status_string.argtypes = [ctypes.c_int]
         L.na_status_string.restype = ctypes.c_char_p
         L.na_last_error.restype = ctypes.c_char_p
         L.na_abi_version.restype = ctypes.c_int32
         for f in ("na_plan_create", "na_plan_destroy", "na_plan_get_stats", "na_plan_get_classes",
-                  "na_plan_get_order", "na_forward", "na_permute"):
+                  "na_plan_get_order", "na_forward", "na_permute", "na_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -247,6 +252,36 @@ class Plan:
                                 ctypes.c_void_p(workspace.data_ptr() if ws_bytes else None),
                                 ws_bytes, ctypes.c_void_p(stream)))
         return out, lse
+
+    def backward(self, q, k, v, out, lse, dout, scale=None, workspace=None, stream=None):
+        """(dq, dk, dv): gradients of sum(out * dout) for the forward's out and
+        lse over the same q, k, v and scale."""
+        import torch
+
+        B, H = int(q.shape[0]), int(q.shape[1])
+        for x in (k, v, out, dout):
+            if tuple(x.shape[:2]) != (B, H):
+                raise ValueError("q, k, v, out, dout must share B and H")
+        if (lse.dtype != torch.float32 or not lse.is_contiguous()
+                or tuple(lse.shape) != (B, H, self.n_tokens)):
+            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.head_dim)
+        dq, dk, dv = (torch.empty_like(x, memory_format=torch.contiguous_format)
+                      for x in (q, k, v))
+        ws_bytes = int(lib().na_backward_workspace_bytes(self._h, B, H))
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        ts = [self._tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"),
+                                              (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+        _check(lib().na_backward(self._h, B, H, *[ctypes.byref(t) for t in ts[:5]],
+                                 ctypes.c_void_p(lse.data_ptr()),
+                                 *[ctypes.byref(t) for t in ts[5:]], float(scale),
+                                 ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
+                                 ctypes.c_void_p(stream)))
+        return dq, dk, dv
 
     def permute(self, x, inverse=False, out=None, stream=None):
         """Rows gathered into the plan's order (or scattered back with inverse)."""

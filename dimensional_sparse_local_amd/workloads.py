@@ -85,3 +85,16 @@ def make_qkv(w: dict, device="cpu", seed: int | None = None):
             x = x.to(torch.bfloat16)
         out.append(x)
     return tuple(out)
+
+
+def make_dout(w: dict, device="cpu", seed: int | None = None):
+    """The upstream gradient for the backward pass: i.i.d. N(0, 1) of shape
+    [B, H, N, D] in fp32 from a generator seeded with 1000 + the workload's
+    seed, rounded like q, k, v."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 + int(w["seed"] if seed is None else seed))
+    shape = (int(w["B"]), int(w["H"]), num_tokens(w), int(w["D"]))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16) if w["dtype"] == "bf16" else x

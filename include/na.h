@@ -176,6 +176,33 @@ na_status na_forward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
                      float scale, uint32_t flags, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Workspace bytes na_backward needs for (B, H): the row sums
+ * delta_i = dout_i . out_i, fp32 [B][H][N] (256-byte multiple). */
+size_t na_backward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H);
+
+/* Gradients of sum_i dout_i . out_i with respect to q, k and v, where out is
+ * the attention of na_forward over the same plan.  The softmax Jacobian is
+ * that of the "pi-Attention" page (gradient analysis of adaptive fusion,
+ * Eq. 23) restricted to the neighbourhood:
+ *     P_ij  = exp(scale q_i . k_j - lse_i),  dP_ij = dout_i . v_j,
+ *     dS_ij = P_ij (dP_ij - delta_i),        delta_i = dout_i . out_i,
+ *     dq_i  = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
+ *     dv_j  = sum_i P_ij dout_i.
+ * Inputs: q, k, v, out, dout (plan dtype and head_dim, layout rules of
+ * na_forward) and lse, the fp32 [B][H][N] output of na_forward for the same
+ * q, k, v and scale.  Outputs dq, dk, dv: every element is written (zero for
+ * keys no query attends and for queries whose neighbourhood is empty); they
+ * must not overlap the inputs.  workspace: >= na_backward_workspace_bytes,
+ * 256-byte aligned, caller-owned; no allocation happens.  bf16 only, head_dim
+ * 64 or 128, (q_block, kv_block) = (128, 64) or (256, 64); other plans return
+ * NA_ERR_UNSUPPORTED.  P and dS are rounded to bf16 before their MFMA
+ * products, accumulation is fp32.  Asynchronous on stream. */
+na_status na_backward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
+                      const na_tensor* k, const na_tensor* v, const na_tensor* out,
+                      const na_tensor* dout, const float* lse, const na_tensor* dq,
+                      const na_tensor* dk, const na_tensor* dv, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Row gather along the plan's order: out[b, h, p, :] = in[b, h, perm[p], :]
  * (inverse = 0) or out[b, h, perm[p], :] = in[b, h, p, :] (inverse = 1), for
  * the plan's dtype and head_dim.  in and out must not overlap. */

@@ -46,6 +46,9 @@ def test_null_arguments():
         == na.NA_ERR_INVALID_ARG
     assert lib.na_permute(None, 1, 1, None, None, 0, None) == na.NA_ERR_INVALID_ARG
     assert lib.na_forward_workspace_bytes(None, 1, 1, 0) == 0
+    assert lib.na_backward(None, 1, 1, None, None, None, None, None, None, None, None, None, 1.0,
+                           None, 0, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_backward_workspace_bytes(None, 1, 1) == 0
 
 
 def test_unknown_flags():

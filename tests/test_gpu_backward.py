@@ -1,0 +1,120 @@
+"""GPU parity of the gradients: na_backward (through the C ABI) against the
+fp64 oracle's gradients on the same bf16 bits of q, k, v and dout.
+
+Tolerance (bf16): relative L2 error <= 1e-2 and max-abs error <= 2e-2 times
+the largest reference magnitude, for each of dq, dk, dv.  Sources of error,
+all from the bf16 arithmetic of the kernel: P and dS are rounded to bf16
+(relative 2^-9 each) before their MFMA products; delta_i = dout_i . out_i is
+taken from the bf16-rounded forward output (relative 2^-9 on out); S, dP and
+the accumulations are fp32.  A rounding error of relative 2^-9 per term
+leaves a relative L2 error of the sums of about 2^-9 ~ 2e-3; the bounds leave
+a factor of five for the cancellation in dP - delta.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dimensional_sparse_local_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-2
+MAX_REL = 2e-2
+
+
+def _na():
+    from dimensional_sparse_local_amd import na
+
+    return na
+
+
+def _grad_case(wl, q_block=0, seed=None):
+    na = _na()
+    print("case %s grid=%s B=%d H=%d D=%d q_block=%d" % (wl["name"], wl["grid"], wl["B"], wl["H"],
+                                                        wl["D"], q_block), flush=True)
+    plan = na.Plan(wl, q_block=q_block)
+    q, k, v = W.make_qkv(wl, device="cuda", seed=seed)
+    g = W.make_dout(wl, device="cuda", seed=seed)
+    scale = W.default_scale(wl)
+    out, lse = plan.forward(q, k, v, scale=scale)
+    dq, dk, dv = plan.backward(q, k, v, out, lse, g, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(wl, q.cpu(), k.cpu(), v.cpu(), g.cpu(), scale)
+    errs = {}
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        a = got.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(a)), "%s: %s not finite" % (wl["name"], name)
+        top = np.max(np.abs(want))
+        rel = np.linalg.norm(a - want) / max(np.linalg.norm(want), 1e-30)
+        mx = np.max(np.abs(a - want)) / max(top, 1e-30)
+        errs[name] = (rel, mx)
+    print("  errors (rel-L2, max-abs / max|ref|): %s" % {k: ("%.2e" % r, "%.2e" % m)
+                                                         for k, (r, m) in errs.items()}, flush=True)
+    for name, (rel, mx) in errs.items():
+        assert rel <= REL_L2 and mx <= MAX_REL, "%s %s: rel-L2 %.3e, max %.3e" % (wl["name"], name,
+                                                                                 rel, mx)
+
+
+SMALL = [
+    W.scaled(W.CONFIGS["na2d_bf16"], name="na2d_small", B=1, H=2, grid=[24, 20],
+             pattern=dict(kind="na", window=[7, 5])),
+    W.scaled(W.CONFIGS["sta3d_bf16"], name="sta3d_small", H=2, grid=[12, 16, 24],
+             pattern=dict(kind="sta", tile=[6, 8, 8], window_tiles=[1, 1, 3])),
+    W.scaled(W.CONFIGS["sta3d_bf16"], name="sta3d_small_d64", H=1, D=64, grid=[6, 16, 40],
+             pattern=dict(kind="sta", tile=[6, 8, 8], window_tiles=[1, 1, 3])),
+    W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_small", B=2, H=2, grid=[32, 32],
+             pattern=dict(kind="band", left=37, right=37)),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="causal_small", H=2, grid=[1000],
+             pattern=dict(kind="band", left=99, right=0)),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="causal_small_d64", H=2, D=64, grid=[333],
+             pattern=dict(kind="band", left=70, right=0)),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="sa3d_ragged", B=1, H=1, grid=[5, 7, 9],
+             pattern=dict(kind="sa", window=[3, 5, 3])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="gna_stride_dil", B=1, H=2, grid=[19, 23],
+             pattern=dict(kind="na", window=[7, 5], stride=[3, 2], dilation=[2, 1])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="blocked_tiled", B=1, H=1, grid=[16, 16],
+             order="tiled", tile=[4, 8], pattern=dict(kind="blocked", window=[4, 8])),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="band_d128_ragged", H=2, grid=[3000],
+             pattern=dict(kind="band", left=600, right=0)),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="na2d_d128_ragged", B=1, H=2, D=128, grid=[40, 50],
+             pattern=dict(kind="na", window=[9, 11])),
+]
+
+
+@pytest.mark.parametrize("q_block", [128, 256])
+@pytest.mark.parametrize("wl", SMALL, ids=[w["name"] for w in SMALL])
+def test_backward_small(wl, q_block):
+    _grad_case(wl, q_block=q_block)
+
+
+def test_backward_empty_rows_and_unattended_keys():
+    """Queries whose window excludes themselves (the first has none) and keys
+    no query attends (the last): zero gradients there, parity elsewhere."""
+    na = _na()
+    wl = W.scaled(W.CONFIGS["causal1d_bf16"], name="strict_past", H=1, grid=[300],
+                  pattern=dict(kind="band", left=10, right=0))
+    d = na.desc_from_workload(wl)
+    d.window[0] = 10
+    d.window_left[0] = 10          # keys [x - 10, x - 1]
+    plan = na.Plan(d)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    g = W.make_dout(wl, device="cuda")
+    out, lse = plan.forward(q, k, v, scale=0.1)
+    dq, dk, dv = plan.backward(q, k, v, out, lse, g, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.all(dq[:, :, 0] == 0)
+    assert torch.all(dk[:, :, -1] == 0) and torch.all(dv[:, :, -1] == 0)
+    ref_wl = W.scaled(wl, pattern=dict(kind="band", left=10, right=-1))
+    ref = oracle.attention_backward(ref_wl, q.cpu(), k.cpu(), v.cpu(), g.cpu(), 0.1)
+    for got, want in zip((dq, dk, dv), ref):
+        a = got.float().cpu().numpy()
+        assert np.linalg.norm(a - want) / np.linalg.norm(want) <= REL_L2
+
+
+def test_backward_full_size_na2d():
+    _grad_case(W.CONFIGS["na2d_bf16"])
+
+
+def test_backward_hilbert_full_grid():
+    _grad_case(W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_full_grid", B=1, H=2))
