@@ -98,6 +98,13 @@ def lib():
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_int32]
+        L.orc_attention_backward_dq_rows.argtypes = [P(_Spec), ctypes.c_int64, ctypes.c_int64,
+                                                     ctypes.c_int64, ctypes.c_int32,
+                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_double, ctypes.c_void_p,
+                                                     ctypes.c_int64, ctypes.c_void_p,
+                                                     ctypes.c_int32]
         L.orc_tile_classes.argtypes = [P(_Spec), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                        P(ctypes.c_int64), ctypes.c_int32]
         L.orc_max_threads.restype = ctypes.c_int32
@@ -277,6 +284,26 @@ def attention_backward(workload: dict, q, k, v, dout, scale: float, threads: int
     if rc != 0:
         raise ValueError("oracle backward failed (%d)" % rc)
     return dq, dk, dv
+
+
+def attention_backward_dq(workload: dict, q, k, v, dout, scale: float, rows, threads: int = 0):
+    """fp64 dq [B, H, len(rows), D] of the same gradients for the listed
+    row-major query tokens only."""
+    s = spec(workload)
+    qa, dt = _raw(q)
+    ka, dk_ = _raw(k)
+    va, dv_ = _raw(v)
+    ga, dg = _raw(dout)
+    assert dt == dk_ == dv_ == dg, "q, k, v, dout must share a dtype"
+    B, H, N, D = qa.shape
+    rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    dq = np.empty((B, H, rows_a.shape[0], D), dtype=np.float64)
+    rc = lib().orc_attention_backward_dq_rows(ctypes.byref(s), B, H, D, dt, _ptr(qa), _ptr(ka),
+                                              _ptr(va), _ptr(ga), float(scale), _ptr(rows_a),
+                                              rows_a.shape[0], _ptr(dq), int(threads))
+    if rc != 0:
+        raise ValueError("oracle backward rows failed (%d)" % rc)
+    return dq
 
 
 def tile_classes(workload: dict, q_block: int, kv_block: int, threads: int = 0):

@@ -350,13 +350,60 @@ int orc_attention(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dt
 /* Gradients of the restricted attention.                                   */
 /* ------------------------------------------------------------------------ */
 
-/* For every query i with a non-empty N(i), in the order of the definition:
+/* Gradient contributions of query i (row-major token) of one (batch, head)
+   slice starting at element `head`, in the order of the definition:
      z_ij = scale q_i . k_j                       (pi-Attention, Eq. 4)
      P_ij = exp(z_ij) / sum_j' exp(z_ij')         (Eq. 2, over N(i))
      dP_ij = dout_i . v_j                         (Eq. 3 is linear in P)
      dz_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')   (softmax Jacobian, Eq. 23)
      dq_i += scale dz_ij k_j,  dk_j += scale dz_ij q_i,  dv_j += P_ij dout_i.
-   Every (batch, head) slice is owned by one thread, so the scatter into dk and
+   dqi receives dq_i (D values, added to); dk / dv (whole slices) may be NULL.
+   nb, p, dp: scratch of N entries; qi, gi: scratch of D entries. */
+static void grad_row(const orc_spec* s, const int64_t* perm, const int64_t* pos, int64_t D,
+                     int32_t dtype, const void* q, const void* k, const void* v,
+                     const void* dout, double scale, int64_t head, int64_t i, double* dqi,
+                     double* dk, double* dv, int64_t* nb, double* p, double* dp, double* qi,
+                     double* gi) {
+    const int64_t n = orc_neighbors(s, perm, pos, i, nb);
+    if (n == 0) return; /* out_i = 0 does not depend on q, k, v */
+    for (int64_t d = 0; d < D; ++d) {
+        qi[d] = load_elem(q, dtype, head + i * D + d);
+        gi[d] = load_elem(dout, dtype, head + i * D + d);
+    }
+    double m = -INFINITY;
+    for (int64_t a = 0; a < n; ++a) {
+        const int64_t kj = head + nb[a] * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += qi[d] * load_elem(k, dtype, kj + d);
+        p[a] = scale * dot;
+        if (p[a] > m) m = p[a];
+    }
+    double l = 0.0;
+    for (int64_t a = 0; a < n; ++a) {
+        p[a] = exp(p[a] - m);
+        l += p[a];
+    }
+    double delta = 0.0;
+    for (int64_t a = 0; a < n; ++a) {
+        p[a] /= l;
+        const int64_t vj = head + nb[a] * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += gi[d] * load_elem(v, dtype, vj + d);
+        dp[a] = dot;
+        delta += p[a] * dot;
+    }
+    for (int64_t a = 0; a < n; ++a) {
+        const double dz = p[a] * (dp[a] - delta);
+        const int64_t j = head + nb[a] * D;
+        for (int64_t d = 0; d < D; ++d) {
+            dqi[d] += scale * dz * load_elem(k, dtype, j + d);
+            if (dk) dk[j + d] += scale * dz * qi[d];
+            if (dv) dv[j + d] += p[a] * gi[d];
+        }
+    }
+}
+
+/* Every (batch, head) slice is owned by one thread, so the scatter into dk and
    dv needs no synchronisation. */
 int orc_attention_backward(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dtype,
                            const void* q, const void* k, const void* v, const void* dout,
@@ -385,46 +432,9 @@ int orc_attention_backward(const orc_spec* s, int64_t B, int64_t H, int64_t D, i
 #pragma omp for schedule(dynamic, 1)
         for (int64_t bh = 0; bh < B * H; ++bh) {
             const int64_t head = bh * N * D;
-            for (int64_t i = 0; i < N; ++i) {
-                const int64_t n = orc_neighbors(s, perm, pos, i, nb);
-                if (n == 0) continue;   /* out_i = 0 does not depend on q, k, v */
-                for (int64_t d = 0; d < D; ++d) {
-                    qi[d] = load_elem(q, dtype, head + i * D + d);
-                    gi[d] = load_elem(dout, dtype, head + i * D + d);
-                }
-                double m = -INFINITY;
-                for (int64_t a = 0; a < n; ++a) {
-                    const int64_t kj = head + nb[a] * D;
-                    double dot = 0.0;
-                    for (int64_t d = 0; d < D; ++d) dot += qi[d] * load_elem(k, dtype, kj + d);
-                    p[a] = scale * dot;
-                    if (p[a] > m) m = p[a];
-                }
-                double l = 0.0;
-                for (int64_t a = 0; a < n; ++a) {
-                    p[a] = exp(p[a] - m);
-                    l += p[a];
-                }
-                double delta = 0.0;
-                for (int64_t a = 0; a < n; ++a) {
-                    p[a] /= l;
-                    const int64_t vj = head + nb[a] * D;
-                    double dot = 0.0;
-                    for (int64_t d = 0; d < D; ++d) dot += gi[d] * load_elem(v, dtype, vj + d);
-                    dp[a] = dot;
-                    delta += p[a] * dot;
-                }
-                double* dqi = dq + head + i * D;
-                for (int64_t a = 0; a < n; ++a) {
-                    const double dz = p[a] * (dp[a] - delta);
-                    const int64_t j = head + nb[a] * D;
-                    for (int64_t d = 0; d < D; ++d) {
-                        dqi[d] += scale * dz * load_elem(k, dtype, j + d);
-                        dk[j + d] += scale * dz * qi[d];
-                        dv[j + d] += p[a] * gi[d];
-                    }
-                }
-            }
+            for (int64_t i = 0; i < N; ++i)
+                grad_row(s, perm, pos, D, dtype, q, k, v, dout, scale, head, i, dq + head + i * D,
+                         dk, dv, nb, p, dp, qi, gi);
         }
         free(gi);
         free(qi);
@@ -435,6 +445,53 @@ int orc_attention_backward(const orc_spec* s, int64_t B, int64_t H, int64_t D, i
     free(pos);
     free(perm);
     return 0;
+}
+
+int orc_attention_backward_dq_rows(const orc_spec* s, int64_t B, int64_t H, int64_t D,
+                                   int32_t dtype, const void* q, const void* k, const void* v,
+                                   const void* dout, double scale, const int64_t* rows,
+                                   int64_t nrows, double* dq, int32_t threads) {
+    const int64_t N = orc_num_tokens(s);
+    int64_t* perm = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (orc_order(s, perm) != 0) {
+        free(perm);
+        return -1;
+    }
+    int64_t* pos = invert(perm, N);
+    int err = 0;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+        double* p = (double*)malloc(sizeof(double) * (size_t)N);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+        double* qi = (double*)malloc(sizeof(double) * (size_t)D);
+        double* gi = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < B * H * nrows; ++t) {
+            const int64_t bh = t / nrows, i = rows[t % nrows];
+            double* out = dq + t * D;
+            for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+            if (i < 0 || i >= N) {
+                err = 1;
+                continue;
+            }
+            grad_row(s, perm, pos, D, dtype, q, k, v, dout, scale, bh * N * D, i, out, NULL, NULL,
+                     nb, p, dp, qi, gi);
+        }
+        free(gi);
+        free(qi);
+        free(dp);
+        free(p);
+        free(nb);
+    }
+    free(pos);
+    free(perm);
+    return err ? -2 : 0;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -105,6 +105,13 @@ int orc_attention_backward(const orc_spec* s, int64_t B, int64_t H, int64_t D, i
                            const void* q, const void* k, const void* v, const void* dout,
                            double scale, double* dq, double* dk, double* dv, int32_t threads);
 
+/* dq of the same gradients for the listed row-major query tokens only:
+   dq [B][H][nrows][D] fp64 (dq_i needs nothing beyond row i's neighbourhood). */
+int orc_attention_backward_dq_rows(const orc_spec* s, int64_t B, int64_t H, int64_t D,
+                                   int32_t dtype, const void* q, const void* k, const void* v,
+                                   const void* dout, double scale, const int64_t* rows,
+                                   int64_t nrows, double* dq, int32_t threads);
+
 /* Tile classes over the sequence order: cls[qt * nkt + kt] in {0 empty,
    1 partial, 2 full}; nqt = ceil(N/q_block), nkt = ceil(N/kv_block).
    *pairs receives the attended-pair count.  Returns 0 on success. */

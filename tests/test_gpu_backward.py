@@ -118,3 +118,51 @@ def test_backward_full_size_na2d():
 
 def test_backward_hilbert_full_grid():
     _grad_case(W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_full_grid", B=1, H=2))
+
+
+def _sample_rows(wl, n_random, seed=0):
+    grid = wl["grid"]
+    corners = set()
+    for c in np.ndindex(*([2] * len(grid))):
+        corners.add(int(np.ravel_multi_index([(g - 1) * b for g, b in zip(grid, c)], grid)))
+    rng = np.random.default_rng(seed)
+    rnd = rng.choice(W.num_tokens(wl), size=n_random, replace=False)
+    return np.array(sorted(corners | set(int(x) for x in rnd)), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["sta3d_bf16", "causal1d_bf16"])
+def test_backward_full_size(name):
+    """Full-size workloads, launched as the benchmark launches them: dq on
+    sampled query rows against the oracle; dk and dv through identities that
+    hold at any size (adding one vector to every key leaves the attention
+    unchanged, so sum_j dk_j = 0; the rows of P sum to one, so
+    sum_j dv_j = sum_i dout_i)."""
+    na = _na()
+    wl = W.CONFIGS[name]
+    print("case %s (full size)" % name, flush=True)
+    plan = na.Plan(wl)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    g = W.make_dout(wl, device="cuda")
+    scale = W.default_scale(wl)
+    out, lse = plan.forward(q, k, v, scale=scale)
+    dq, dk, dv = plan.backward(q, k, v, out, lse, g, scale=scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(wl, 24, seed=wl["seed"])
+    heads = [0, int(wl["H"]) - 1]
+    sub = lambda x: x[:, heads].contiguous()
+    ref = oracle.attention_backward_dq(wl, sub(q).cpu(), sub(k).cpu(), sub(v).cpu(), sub(g).cpu(),
+                                       scale, rows)
+    got = dq[:, heads][:, :, rows].float().cpu().numpy()
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    mx = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+    print("  dq rows: rel-L2 %.2e max %.2e" % (rel, mx), flush=True)
+    assert rel <= REL_L2 and mx <= MAX_REL
+    sdv = dv.double().sum(dim=2)
+    sg = g.double().sum(dim=2)
+    e_dv = (torch.linalg.norm(sdv - sg) / torch.linalg.norm(sg)).item()
+    sdk = dk.double().sum(dim=2)
+    scale_dk = (dk.double().pow(2).sum(dim=2).sqrt()).norm().item()
+    e_dk = torch.linalg.norm(sdk).item() / scale_dk
+    print("  sum dv vs sum dout: %.2e   |sum dk| / sqrt(sum |dk|^2): %.2e" % (e_dv, e_dk), flush=True)
+    assert e_dv <= 1e-3
+    assert e_dk <= 2e-2

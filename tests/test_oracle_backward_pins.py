@@ -139,3 +139,14 @@ def test_backward_bf16_inputs_are_upcast_exactly():
     b = oracle.attention_backward(wl, *[x.double() for x in xs], 0.25)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_backward_dq_rows_subset():
+    """dq of selected rows equals the same rows of the full gradient."""
+    wl = MASKED[3]
+    N = W.num_tokens(wl)
+    q, k, v, g = (_rand((1, 1, N, 8), s) for s in (61, 62, 63, 64))
+    dq, _, _ = oracle.attention_backward(wl, q, k, v, g, 0.4)
+    rows = np.array([0, 7, 31, N - 1])
+    sub = oracle.attention_backward_dq(wl, q, k, v, g, 0.4, rows)
+    assert np.array_equal(sub, dq[:, :, rows])
