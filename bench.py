@@ -47,9 +47,9 @@ def kernel_signature() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    src = os.path.join(ROOT, "dimensional_sparse_local_amd", "csrc", "attn_fwd.hip")
-    with open(src, "rb") as f:
-        h.update(f.read())
+    for name in ("attn_fwd.hip", "attn_common.h"):
+        with open(os.path.join(ROOT, "dimensional_sparse_local_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -95,6 +95,10 @@ def main():
     ap.add_argument("--permute-passes", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                    help="time the forward (default) or the backward pass (dq, dk, dv from the "
+                         "forward's out and lse; effective flops 10 * D per attended pair: the "
+                         "recomputed score and the dP, dV, dK, dQ products)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the row-permute kernel over 268,435,456 bytes (read once, "
                          "written once): the known-size copy that calibrates HBM counters")
@@ -141,6 +145,19 @@ def main():
     def step():
         plan.forward(q, k, v, out=out, lse=lse, scale=scale, permute_passes=args.permute_passes)
 
+    if args.which == "backward":
+        if args.permute_passes:
+            raise SystemExit("--permute-passes applies to the forward pass only")
+        dout = W.make_dout(wl, device=dev)
+        step()
+        grads = tuple(torch.empty_like(x) for x in (q, k, v))
+        ws = torch.empty(int(na.lib().na_backward_workspace_bytes(plan._h, B, H)),
+                         dtype=torch.uint8, device=dev)
+        flops = flops * 10 // 4
+
+        def step():
+            plan.backward(q, k, v, out, lse, dout, scale=scale, grads=grads, workspace=ws)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -159,13 +176,14 @@ def main():
     peak = PEAK_TFLOPS[wl["dtype"]]
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.which == "forward":
         log("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
         cpu = cpu_baseline(wl, q, k, v, scale, args.cpu_seconds)
 
     sig = kernel_signature()
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "forward" else
+        "effective TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, backward pass",
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -183,10 +201,11 @@ def main():
                    "attended_pairs_per_head": plan.stats["attended_pairs"],
                    "effective_flops_per_step": flops,
                    "pct_of_peak": round(100.0 * tflops / peak, 2),
-                   "permute_passes": bool(args.permute_passes)},
+                   "permute_passes": bool(args.permute_passes), "pass": args.which},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": read_traffic(sig), "kernel_sig": sig},
+                     "traffic": read_traffic(sig) if args.which == "forward" else None,
+                     "kernel_sig": sig},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -253,9 +253,11 @@ class Plan:
                                 ws_bytes, ctypes.c_void_p(stream)))
         return out, lse
 
-    def backward(self, q, k, v, out, lse, dout, scale=None, workspace=None, stream=None):
+    def backward(self, q, k, v, out, lse, dout, scale=None, grads=None, workspace=None,
+                 stream=None):
         """(dq, dk, dv): gradients of sum(out * dout) for the forward's out and
-        lse over the same q, k, v and scale."""
+        lse over the same q, k, v and scale.  grads: optional preallocated
+        (dq, dk, dv)."""
         import torch
 
         B, H = int(q.shape[0]), int(q.shape[1])
@@ -267,8 +269,10 @@ class Plan:
             raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
         if scale is None:
             scale = 1.0 / math.sqrt(self.head_dim)
-        dq, dk, dv = (torch.empty_like(x, memory_format=torch.contiguous_format)
-                      for x in (q, k, v))
+        if grads is None:
+            grads = tuple(torch.empty_like(x, memory_format=torch.contiguous_format)
+                          for x in (q, k, v))
+        dq, dk, dv = grads
         ws_bytes = int(lib().na_backward_workspace_bytes(self._h, B, H))
         if workspace is None:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
