@@ -4,8 +4,10 @@ batch of synthetic input, by default the 3-D sliding-tile workload (batch 1,
 
 Prints ONE JSON line: effective TFLOP/s (only unmasked QK^T + PV flops,
 4 * D * attended pairs * B * H per step), the roofline of the attention kernel
-(MFMA bound, MI355X dense bf16 peak), and the fp64 CPU oracle timed on a
-bounded sample of the same workload as a reported baseline.
+(MFMA bound against the MI355X dense peak of the dtype, or HBM bound against
+8 TB/s when moving every tensor once takes longer than the flops at peak),
+and the fp64 CPU oracle timed on a bounded sample of the same workload as a
+reported baseline.
 """
 from __future__ import annotations
 
@@ -21,6 +23,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, 3D sliding-tile attn"
 PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA (published)
+PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E (published)
+ELEM_BYTES = {"bf16": 2, "fp32": 4}
 PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_fwd_sta3d_pmc.md")
 
 
@@ -28,15 +32,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def read_traffic(kernel_sig: str):
+def read_traffic(kernel_sig: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
-    was taken on the current kernel source (null otherwise)."""
+    was taken on the current kernel source and this workload (null otherwise)."""
     try:
         with open(PROFILE_PMC) as f:
             for line in f:
                 if line.startswith("traffic_json:"):
                     d = json.loads(line.split(":", 1)[1])
-                    if d.get("kernel_sig") == kernel_sig:
+                    if d.get("kernel_sig") == kernel_sig and d.get("workload") == workload:
                         return d.get("bytes_per_launch")
     except OSError:
         pass
@@ -129,7 +133,7 @@ def main():
         return
 
     name = args.workload or W.HEADLINE
-    wl = W.CONFIGS[name]
+    wl = W.ALL[name]
     B, H, D = int(wl["B"]), int(wl["H"]), int(wl["D"])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -174,6 +178,14 @@ def main():
     log("bench: %.3f ms/step" % ms)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl["dtype"]]
+    # Algorithmic HBM bytes per step: every tensor read or written once
+    # (forward: q, k, v in, out and fp32 lse out; backward: q, k, v, out, dout
+    # and lse in, dq, dk, dv out).
+    n_rows = B * H * plan.n_tokens
+    row_tensors = 4 if args.which == "forward" else 8
+    alg_bytes = n_rows * (row_tensors * D * ELEM_BYTES[wl["dtype"]] + 4)
+    hbm_bound = alg_bytes / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12)
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline and args.which == "forward":
@@ -181,9 +193,21 @@ def main():
         cpu = cpu_baseline(wl, q, k, v, scale, args.cpu_seconds)
 
     sig = kernel_signature()
+    if name == W.HEADLINE and args.which == "forward":
+        metric = METRIC
+    else:
+        metric = "effective TFLOP/s (unmasked FLOPs), %s%s" % (
+            wl.get("note", name), ", backward pass" if args.which == "backward" else "")
+    traffic = read_traffic(sig, name) if args.which == "forward" else None
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4)}
+    roof.update({"traffic": traffic, "algorithmic_bytes": alg_bytes, "kernel_sig": sig})
     line = {
-        "metric": METRIC if args.which == "forward" else
-        "effective TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, backward pass",
+        "metric": metric,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -202,10 +226,7 @@ def main():
                    "effective_flops_per_step": flops,
                    "pct_of_peak": round(100.0 * tflops / peak, 2),
                    "permute_passes": bool(args.permute_passes), "pass": args.which},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": read_traffic(sig) if args.which == "forward" else None,
-                     "kernel_sig": sig},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -21,35 +21,95 @@ namespace {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+// Hilbert order over any rows x cols grid.  The pages give the curve only for
+// power-of-two squares (and no orientation); this is the library's reading for
+// every grid: blocks are cut the way the classic curve cuts a square (four
+// quadrants in a U: near-left travelling across, far-left and far-right
+// travelling along, near-right travelling back), blocks more than twice as long
+// as wide are cut into two halves along their travel direction instead, and
+// the cut points are even wherever possible so that consecutive cells are
+// 4-neighbours whenever the block's start and end corners allow it (when they
+// cannot, a 3 x 2 end block takes one diagonal step).  On power-of-two squares
+// this is exactly the classic curve from (0, 0) to (0, n - 1).
+//
+// A block is (origin, travel direction a, turn direction b, w cells along a,
+// h along b); its walk starts at the origin and ends w - 1 steps along a.
+struct CurveBlock {
+    int64_t r, c;     // origin cell
+    int64_t ar, ac;   // unit travel direction
+    int64_t br, bc;   // unit turn direction
+    int64_t w, h;
+};
 
-// Hilbert curve index -> cell, by the standard bit-by-bit construction: at each
-// scale s the two bits of the index pick a quadrant, and the coordinates built
-// so far are reflected / transposed into that quadrant's frame.  With row = y
-// and col = x the curve starts at (0, 0) and ends at (0, n - 1).
-void hilbert_cell(int64_t n, int64_t d, int64_t* row, int64_t* col) {
-    int64_t x = 0, y = 0, t = d;
-    for (int64_t s = 1; s < n; s *= 2) {
-        const int64_t rx = 1 & (t / 2);
-        const int64_t ry = 1 & (t ^ rx);
-        if (ry == 0) {
-            if (rx == 1) {
-                x = s - 1 - x;
-                y = s - 1 - y;
-            }
-            std::swap(x, y);
+int64_t even_cut(int64_t len) {  // even cut near len / 2, in [2, len - 2]
+    return std::min(std::max<int64_t>(2 * ((len + 2) / 4), 2), len - 2);
+}
+
+void hilbert_order(int64_t rows, int64_t cols, std::vector<int32_t>& perm) {
+    perm.clear();
+    perm.reserve(rows * cols);
+    auto put = [&](int64_t r, int64_t c) { perm.push_back((int32_t)(r * cols + c)); };
+    std::vector<CurveBlock> todo;  // processed last-in first-out: children pushed in reverse
+    todo.push_back({0, 0, 0, 1, 1, 0, cols, rows});
+    while (!todo.empty()) {
+        const CurveBlock k = todo.back();
+        todo.pop_back();
+        if (k.h == 1 || k.w == 1) {
+            // a single run; a width-1 block (only a one-column grid) runs along b
+            const int64_t n = k.h == 1 ? k.w : k.h;
+            const int64_t dr = k.h == 1 ? k.ar : k.br, dc = k.h == 1 ? k.ac : k.bc;
+            for (int64_t t = 0; t < n; ++t) put(k.r + t * dr, k.c + t * dc);
+            continue;
         }
-        x += s * rx;
-        y += s * ry;
-        t /= 4;
+        if (k.h == 2 && k.w <= 3) {
+            // 2 x 2: across, along, back.  3 x 2: across, diagonal back to the
+            // second column, then the 2 x 2 pattern.
+            put(k.r, k.c);
+            put(k.r + k.br, k.c + k.bc);
+            int64_t r = k.r + k.ar, c = k.c + k.ac;
+            if (k.w == 3) {
+                put(r, c);
+                put(r + k.br, c + k.bc);
+                r += k.ar;
+                c += k.ac;
+                put(r + k.br, c + k.bc);
+                put(r, c);
+            } else {
+                put(r + k.br, c + k.bc);
+                put(r, c);
+            }
+            continue;
+        }
+        if (k.h == 2 || k.w > 2 * k.h) {
+            const int64_t w1 = even_cut(k.w);
+            todo.push_back({k.r + w1 * k.ar, k.c + w1 * k.ac, k.ar, k.ac, k.br, k.bc, k.w - w1, k.h});
+            todo.push_back({k.r, k.c, k.ar, k.ac, k.br, k.bc, w1, k.h});
+            continue;
+        }
+        // Quadrants.  Narrow blocks (w <= 3) keep one far row; otherwise the far
+        // part is about half the block (no deeper than half its width) and the
+        // near part is rounded to an even depth.
+        int64_t w1 = k.w - 1, hn = k.h - 1;
+        if (k.w > 3) {
+            w1 = even_cut(k.w);
+            hn = k.h - std::max<int64_t>(1, std::min(k.h / 2, k.w / 2));
+            if (hn & 1) hn += (k.h - hn >= 2) ? 1 : -1;
+        }
+        const int64_t hf = k.h - hn, w2 = k.w - w1;
+        // pushed in reverse visiting order
+        todo.push_back({k.r + (k.w - 1) * k.ar + (hn - 1) * k.br, k.c + (k.w - 1) * k.ac + (hn - 1) * k.bc,
+                        -k.br, -k.bc, -k.ar, -k.ac, hn, w2});
+        todo.push_back({k.r + w1 * k.ar + hn * k.br, k.c + w1 * k.ac + hn * k.bc, k.ar, k.ac, k.br, k.bc,
+                        w2, hf});
+        todo.push_back({k.r + hn * k.br, k.c + hn * k.bc, k.ar, k.ac, k.br, k.bc, w1, hf});
+        todo.push_back({k.r, k.c, k.br, k.bc, k.ar, k.ac, hn, w1});
     }
-    *row = y;
-    *col = x;
 }
 
 struct Axis {
     int64_t L, w, left, stride, dil;
     bool clamp;
+    int64_t shift;  // stride-group phase
 };
 
 // [lo, hi) of the keys of coordinate x on one axis, in axis coordinates; with
@@ -58,7 +118,7 @@ void axis_window(const Axis& a, int64_t x, int32_t* lo, int32_t* hi) {
     const int64_t g = x % a.dil;
     const int64_t xl = x / a.dil;
     const int64_t Lg = ceil_div(a.L - g, a.dil);
-    const int64_t c = (xl / a.stride) * a.stride + a.stride / 2;
+    const int64_t c = ((xl + a.shift) / a.stride) * a.stride - a.shift + a.stride / 2;
     int64_t s, e;
     if (a.clamp) {
         if (a.w >= Lg) {
@@ -136,11 +196,9 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
         return NA_ERR_INVALID_ARG;
     }
     const int pdims = d.order == NA_ORDER_HILBERT ? 1 : d.ndim;
-    if (d.order == NA_ORDER_HILBERT) {
-        if (d.ndim != 2 || d.grid[0] != d.grid[1] || !is_pow2(d.grid[0])) {
-            na_set_error("Hilbert order needs a square power-of-two 2-D grid");
-            return NA_ERR_UNSUPPORTED;
-        }
+    if (d.order == NA_ORDER_HILBERT && d.ndim != 2) {
+        na_set_error("Hilbert order needs a 2-D grid");
+        return NA_ERR_UNSUPPORTED;
     }
     if (d.order == NA_ORDER_TILED) {
         for (int i = 0; i < d.ndim; ++i)
@@ -153,13 +211,14 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
     Axis ax[3];
     for (int i = 0; i < 3; ++i) {
         if (i >= pdims) {
-            ax[i] = Axis{1, 1, 0, 1, 1, true};
+            ax[i] = Axis{1, 1, 0, 1, 1, true, 0};
             p->plen[i] = 1;
             p->left[i] = 0;
             p->clamp[i] = 1;
             d.window[i] = 1;
             d.window_left[i] = 0;
             d.stride[i] = 1;
+            d.shift[i] = 0;
             d.dilation[i] = 1;
             d.causal[i] = 0;
             d.boundary[i] = NA_BOUND_CLAMP;
@@ -174,6 +233,10 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
             // a group wider than its window would not see all of itself
             na_set_error("stride[%d] (%d) must not exceed window[%d] (%d)", i, d.stride[i], i,
                          d.window[i]);
+            return NA_ERR_INVALID_ARG;
+        }
+        if (d.shift[i] < 0 || d.shift[i] >= d.stride[i]) {
+            na_set_error("shift[%d] (%d) must lie in [0, stride[%d])", i, d.shift[i], i);
             return NA_ERR_INVALID_ARG;
         }
         if (d.causal[i] != 0 && d.causal[i] != 1) {
@@ -197,7 +260,7 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
         }
         d.window_left[i] = (int32_t)left;
         ax[i] = Axis{L, d.window[i], left, d.stride[i], d.dilation[i],
-                     d.boundary[i] == NA_BOUND_CLAMP};
+                     d.boundary[i] == NA_BOUND_CLAMP, d.shift[i]};
         p->plen[i] = (int32_t)L;
         p->left[i] = (int32_t)left;
         p->clamp[i] = d.boundary[i] == NA_BOUND_CLAMP;
@@ -213,13 +276,13 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
         for (int64_t i = 0; i < N; ++i) p->perm[i] = (int32_t)i;
         p->identity_order = true;
     } else if (d.order == NA_ORDER_HILBERT) {
-        const int64_t n = d.grid[0];
-        for (int64_t t = 0; t < N; ++t) {
-            int64_t r, c;
-            hilbert_cell(n, t, &r, &c);
-            p->perm[t] = (int32_t)(r * n + c);
-        }
-        p->identity_order = false;
+        hilbert_order(d.grid[0], d.grid[1], p->perm);
+        p->identity_order = true;  // a one-row or one-column grid
+        for (int64_t i = 0; i < N; ++i)
+            if (p->perm[i] != i) {
+                p->identity_order = false;
+                break;
+            }
     } else {
         const int64_t g1 = d.grid[1], g2 = d.grid[2];
         const int64_t nt0 = ceil_div(d.grid[0], d.tile[0]);

@@ -33,7 +33,7 @@ class Desc(ctypes.Structure):
         ("ndim", ctypes.c_int32), ("grid", I3), ("order", ctypes.c_int32), ("tile", I3),
         ("window", I3), ("window_left", I3), ("stride", I3), ("dilation", I3), ("causal", I3),
         ("boundary", I3), ("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
-        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("shift", I3),
     ]
 
 
@@ -59,6 +59,7 @@ _STATUS = {NA_ERR_INVALID_ARG: "invalid argument", NA_ERR_UNSUPPORTED: "unsuppor
            NA_ERR_PLAN_MISMATCH: "plan mismatch"}
 
 _lib = None
+ABI_VERSION = 2  # NA_ABI_VERSION of include/na.h that Desc mirrors
 
 
 def lib():
@@ -92,6 +93,9 @@ def lib():
         for f in ("na_plan_create", "na_plan_destroy", "na_plan_get_stats", "na_plan_get_classes",
                   "na_plan_get_order", "na_forward", "na_permute", "na_backward"):
             getattr(L, f).restype = ctypes.c_int
+        if L.na_abi_version() != ABI_VERSION:
+            raise RuntimeError("libna.so has ABI version %d, this binding expects %d (rebuild)"
+                               % (L.na_abi_version(), ABI_VERSION))
         _lib = L
     return _lib
 
@@ -125,6 +129,7 @@ def desc_from_workload(w: dict, q_block: int = 0, kv_block: int = 0) -> Desc:
         if kind in ("na", "sa"):
             d.window[i] = int(pat["window"][i])
             d.stride[i] = int(pat.get("stride", [1, 1, 1])[i])
+            d.shift[i] = int(pat.get("shift", [0, 0, 0])[i])
             d.dilation[i] = int(pat.get("dilation", [1, 1, 1])[i])
             d.boundary[i] = NA_BOUND_CLAMP if kind == "na" else NA_BOUND_TRUNCATE
         elif kind == "band":
@@ -133,8 +138,10 @@ def desc_from_workload(w: dict, q_block: int = 0, kv_block: int = 0) -> Desc:
             d.window_left[i] = left
             d.boundary[i] = NA_BOUND_TRUNCATE
         elif kind == "blocked":
-            # non-overlapping windows: a window of w whose stride is w, cut at the end
+            # non-overlapping windows: a window of w whose stride is w, cut at the end;
+            # shifted windows move the group boundaries back by `shift`
             d.window[i] = d.stride[i] = int(pat["window"][i])
+            d.shift[i] = int(pat.get("shift", [0, 0, 0])[i])
             d.boundary[i] = NA_BOUND_TRUNCATE
         elif kind == "sta":
             # sliding tile attention: window of (tiles * tile) positions moving one

@@ -8,18 +8,21 @@ Pattern vocabulary (per grid dimension unless noted):
 
 * ``na``      window of ``window[d]`` positions centred on the query and shifted
               inside the grid at the borders (neighbourhood attention);
-              optional ``stride`` (groups sharing one window) and ``dilation``.
+              optional ``stride`` (groups sharing one window), ``shift`` (the
+              groups' phase: they start at positions congruent to -shift) and
+              ``dilation``.
 * ``sa``      the same window cut at the grid borders instead of shifted
               (slide attention, zero padding).
 * ``band``    1-D only: keys in [x - left, x + right] cut at the ends
               (bidirectional band; causal when right = 0).
-* ``blocked`` non-overlapping windows of ``window[d]`` positions.
+* ``blocked`` non-overlapping windows of ``window[d]`` positions; optional
+              ``shift[d]`` moves the window boundaries back (shifted windows).
 * ``sta``     sliding tile attention: tiles of ``tile[d]`` positions; the query's
               tile attends ``window_tiles[d]`` whole tiles shifted inside.
 
 Orders: ``row_major``; ``tiled`` (tile by tile with tile extents ``tile``,
-row-major inside); ``hilbert`` (2-D square power-of-two grid; the pattern is
-then 1-D over the position along the curve).
+row-major inside); ``hilbert`` (2-D grid of any size along a Hilbert curve; the
+pattern is then 1-D over the position along the curve).
 """
 from __future__ import annotations
 
@@ -49,6 +52,47 @@ CONFIGS = {
         pattern=dict(kind="band", left=4095, right=0), seed=5,
         note="1-D causal sliding window, 32768 tokens, 4096 keys including self"),
 }
+
+# The Hilbert page's kernel benchmarks ("Hilbert-Guided Sparse Local Attention",
+# Tables 1-3): batch 16, 2 heads, head_dim 64, patterns formed on the curve.  A
+# k x k window becomes k*k consecutive curve positions (HWA: non-overlapping
+# windows; HSWA: the same windows shifted by half a window); a k x k slide or
+# neighbourhood kernel becomes k*k positions around the query (HSA: band of
+# radius (k*k - 1) / 2 cut at the ends; HNA: window of k*k shifted inside).
+# 56 x 56 and 96 x 96 are not powers of two: they run on the generalised curve.
+HILBERT_PAGE = {
+    "hwa96_bf16": dict(
+        name="hwa96_bf16", B=16, H=2, D=64, dtype="bf16", grid=[96, 96], order="hilbert",
+        pattern=dict(kind="blocked", window=[64]), seed=11,
+        note="Hilbert window attention, 96x96 input, 8x8 window (Table 1)"),
+    "hswa96_bf16": dict(
+        name="hswa96_bf16", B=16, H=2, D=64, dtype="bf16", grid=[96, 96], order="hilbert",
+        pattern=dict(kind="blocked", window=[64], shift=[32]), seed=12,
+        note="Hilbert shifted window attention, 96x96 input, 8x8 window shifted by 32"),
+    "hwa128_bf16": dict(
+        name="hwa128_bf16", B=16, H=2, D=64, dtype="bf16", grid=[128, 128], order="hilbert",
+        pattern=dict(kind="blocked", window=[256]), seed=13,
+        note="Hilbert window attention, 128x128 input, 16x16 window (Tables 1-2)"),
+    "hsa56_bf16": dict(
+        name="hsa56_bf16", B=16, H=2, D=64, dtype="bf16", grid=[56, 56], order="hilbert",
+        pattern=dict(kind="band", left=24, right=24), seed=14,
+        note="Hilbert slide attention, 56x56 input, 7x7 kernel (Table 3)"),
+    "hna56_bf16": dict(
+        name="hna56_bf16", B=16, H=2, D=64, dtype="bf16", grid=[56, 56], order="hilbert",
+        pattern=dict(kind="na", window=[49]), seed=15,
+        note="Hilbert neighbourhood attention, 56x56 input, 7x7 kernel (Table 3)"),
+    "hsa96_bf16": dict(
+        name="hsa96_bf16", B=16, H=2, D=64, dtype="bf16", grid=[96, 96], order="hilbert",
+        pattern=dict(kind="band", left=24, right=24), seed=16,
+        note="Hilbert slide attention, 96x96 input, 7x7 kernel (Table 3)"),
+    "hna96_bf16": dict(
+        name="hna96_bf16", B=16, H=2, D=64, dtype="bf16", grid=[96, 96], order="hilbert",
+        pattern=dict(kind="na", window=[49]), seed=17,
+        note="Hilbert neighbourhood attention, 96x96 input, 7x7 kernel (Table 3)"),
+}
+
+# Every named workload.
+ALL = {**CONFIGS, **HILBERT_PAGE}
 
 # The workload the benchmark times by default (the headline metric's config).
 HEADLINE = "sta3d_bf16"

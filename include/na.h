@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define NA_ABI_VERSION 1
+#define NA_ABI_VERSION 2
 
 typedef enum {
     NA_OK = 0,
@@ -65,9 +65,14 @@ typedef enum {
 enum {
     NA_ORDER_ROW_MAJOR = 0, /* row-major grid order */
     NA_ORDER_TILED = 1,     /* tile by tile (tile extents in na_plan_desc.tile), row-major inside */
-    NA_ORDER_HILBERT = 2    /* 2-D square power-of-two grid along a Hilbert curve that starts at
-                               (row 0, col 0) and ends at (row 0, col n-1); the pattern is 1-D over
-                               the curve position */
+    NA_ORDER_HILBERT = 2    /* 2-D grid along a Hilbert curve that starts at (row 0, col 0) and
+                               ends at (row 0, cols-1); the pattern is 1-D over the curve position.
+                               On power-of-two squares the classic curve; on any other rows x cols
+                               grid its generalisation: blocks cut into the classic four-quadrant U
+                               (or, when more than twice as long as wide, into two halves along the
+                               travel direction) at even cut points where possible, so every step
+                               is to a 4-neighbour unless cols is odd and rows even (then exactly
+                               one step is diagonal) */
 };
 
 /* Border rule of a pattern dimension. */
@@ -93,7 +98,7 @@ enum { NA_BF16 = 0, NA_F32 = 1 };
  * NA_ORDER_HILBERT where there is one pattern dimension: the curve position,
  * of length N.  For pattern dimension d with length L, a query at coordinate x
  * attends the keys y with
- *     c   = (x' / stride) * stride + stride / 2       (x' = x / dilation)
+ *     c   = ((x' + shift) / stride) * stride - shift + stride / 2   (x' = x / dilation)
  *     lo  = c - left, hi = lo + window                 (left = window_left, or window / 2,
  *                                                       or window - 1 when causal)
  *     clamp:    [lo, hi) shifted to lie inside [0, L'), or all of [0, L') if window >= L'
@@ -118,6 +123,10 @@ typedef struct {
     int32_t kv_block;       /* key/value tile length in tokens, 0 = library default */
     int32_t head_dim;       /* D */
     int32_t dtype;          /* NA_BF16 or NA_F32 */
+    int32_t shift[3];       /* phase of the stride groups, 0 <= shift < stride: groups are
+                               [k*stride - shift, (k+1)*stride - shift).  With stride = window and
+                               truncation, shift = window / 2 gives shifted (Swin-style) windows,
+                               the shifted-window form of the Hilbert page's window attention */
 } na_plan_desc;
 
 typedef struct {
@@ -142,7 +151,7 @@ typedef struct na_plan_s* na_plan_t;
  * per-token mask tables to the current device.  The plan owns all of it and is
  * immutable afterwards; it may be used from several streams at once.
  * Returns NA_ERR_INVALID_ARG for a malformed descriptor, NA_ERR_UNSUPPORTED for
- * a Hilbert order on a grid that is not a square power of two. */
+ * a Hilbert order on a grid that is not 2-D. */
 na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* plan);
 
 /* Release a plan (host and device memory).  The caller must first make sure

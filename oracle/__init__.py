@@ -44,6 +44,7 @@ class _Rule(ctypes.Structure):
         ("dil", ctypes.c_int64),
         ("tile", ctypes.c_int64),
         ("wt", ctypes.c_int64),
+        ("shift", ctypes.c_int64),
     ]
 
 
@@ -81,6 +82,7 @@ def lib():
         L.orc_num_tokens.restype = ctypes.c_int64
         L.orc_order.argtypes = [P(_Spec), ctypes.c_void_p]
         L.orc_hilbert.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+        L.orc_hilbert_grid.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         L.orc_rule_set.argtypes = [P(_Rule), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         L.orc_rule_set.restype = ctypes.c_int64
         L.orc_neighbors.argtypes = [P(_Spec), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -130,11 +132,13 @@ def _rule_for(pattern: dict, d: int) -> _Rule:
         r.clamp = 1 if kind == "na" else 0
         r.stride = int(pattern.get("stride", [1, 1, 1])[d])
         r.dil = int(pattern.get("dilation", [1, 1, 1])[d])
+        r.shift = int(pattern.get("shift", [0, 0, 0])[d])
     elif kind == "band":
         left, right = int(pattern["left"]), int(pattern["right"])
         r.kind, r.clamp, r.w, r.left = ORC_WINDOW, 0, left + right + 1, left
     elif kind == "blocked":
         r.kind, r.w = ORC_BLOCKED, int(pattern["window"][d])
+        r.shift = int(pattern.get("shift", [0, 0, 0])[d])
     elif kind == "sta":
         r.kind = ORC_STA
         r.tile = int(pattern["tile"][d])
@@ -188,6 +192,14 @@ def hilbert(n: int) -> np.ndarray:
     perm = np.empty(n * n, dtype=np.int64)
     if lib().orc_hilbert(n, _ptr(perm)) != 0:
         raise ValueError("Hilbert order needs a power-of-two side")
+    return perm
+
+
+def hilbert_grid(rows: int, cols: int) -> np.ndarray:
+    """Generalised Hilbert curve over a rows x cols grid (perm[p] = row * cols + col)."""
+    perm = np.empty(rows * cols, dtype=np.int64)
+    if lib().orc_hilbert_grid(rows, cols, _ptr(perm)) != 0:
+        raise ValueError("grid must be at least 1 x 1")
     return perm
 
 

@@ -64,8 +64,8 @@ static int64_t extent(const orc_spec* s, int d) { return d < s->ndim ? s->grid[d
    x - left).  With clamp the window is shifted to lie inside the axis (the
    neighbourhood-attention border rule); without it the window is cut at the
    axis ends (positions outside are invalid and dropped).  Stride: positions are
-   grouped `stride` at a time and each group uses the window of its middle
-   position.  Dilation: only positions congruent to x modulo `dil` take part,
+   grouped `stride` at a time (groups start at positions congruent to -shift)
+   and each group uses the window of its middle position.  Dilation: only positions congruent to x modulo `dil` take part,
    and the rule runs in the coordinates of that sub-grid. */
 static int64_t window_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out) {
     const int64_t dil = r->dil > 0 ? r->dil : 1;
@@ -74,7 +74,8 @@ static int64_t window_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out)
     const int64_t xl = x / dil;                /* coordinate inside it */
     const int64_t Lg = ceil_div(L - g, dil);   /* its length */
     /* group leader; with stride 1 every position leads its own group */
-    const int64_t centre = (xl / stride) * stride + stride / 2;
+    const int64_t first = ((xl + r->shift) / stride) * stride - r->shift; /* group start */
+    const int64_t centre = first + stride / 2;
     int64_t lo, hi;
     if (r->clamp) {
         if (r->w >= Lg) {
@@ -93,10 +94,14 @@ static int64_t window_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out)
     return n;
 }
 
-/* Non-overlapping windows of w positions; the last one may be shorter. */
+/* Non-overlapping windows of w positions; the first and last may be shorter.
+   Window k covers [k*w - shift, (k+1)*w - shift): shift = 0 is plain window
+   attention, shift > 0 the shifted windows that let neighbouring windows
+   exchange information ("Hilbert-Guided Sparse Local Attention", Key
+   Contributions: windows shifted along the 1-D sequence). */
 static int64_t blocked_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out) {
-    const int64_t lo = (x / r->w) * r->w;
-    const int64_t hi = imin(lo + r->w, L);
+    const int64_t lo = imax(((x + r->shift) / r->w) * r->w - r->shift, 0);
+    const int64_t hi = imin(((x + r->shift) / r->w + 1) * r->w - r->shift, L);
     int64_t n = 0;
     for (int64_t t = lo; t < hi; ++t) out[n++] = t;
     return n;
@@ -164,6 +169,108 @@ int orc_hilbert(int64_t n, int64_t* perm) {
     return 0;
 }
 
+/* Generalised Hilbert curve over any rows x cols grid.  The pages name no
+   curve for grids that are not power-of-two squares; this construction is a
+   reading (documented with the library): it is the classic curve above on
+   power-of-two squares, and elsewhere splits a block into the same four
+   quadrants visited in the same U, or into two halves along its travel
+   direction when the block is more than twice as long as it is wide, with
+   split points chosen so that every step moves to a 4-neighbour whenever a
+   path with the block's two end corners allows it.
+
+   walk() emits the w x h block of cells o + i*a + j*b (0 <= i < w, 0 <= j < h;
+   a and b unit vectors in (row, col)), starting at o and, when w >= 2, ending
+   at o + (w-1)*a. */
+typedef struct {
+    int64_t cols;
+    int64_t* perm;
+    int64_t k;
+} walk_out;
+
+static void walk_emit(walk_out* out, int64_t r, int64_t c) {
+    out->perm[out->k++] = r * out->cols + c;
+}
+
+/* Even split near the middle of a length >= 4: 2 * floor((w + 2) / 4), kept in
+   [2, w - 2]. */
+static int64_t even_half(int64_t w) {
+    int64_t h = 2 * ((w + 2) / 4);
+    if (h < 2) h = 2;
+    if (h > w - 2) h = w - 2;
+    return h;
+}
+
+static void walk(walk_out* out, int64_t r, int64_t c, int64_t ar, int64_t ac, int64_t br,
+                 int64_t bc, int64_t w, int64_t h) {
+    if (h == 1) { /* a straight run along a */
+        for (int64_t i = 0; i < w; ++i) walk_emit(out, r + i * ar, c + i * ac);
+        return;
+    }
+    if (w == 1) { /* only for a one-column grid: straight down b */
+        for (int64_t j = 0; j < h; ++j) walk_emit(out, r + j * br, c + j * bc);
+        return;
+    }
+    if (h == 2 && w == 2) { /* the U of the classic curve */
+        walk_emit(out, r, c);
+        walk_emit(out, r + br, c + bc);
+        walk_emit(out, r + ar + br, c + ac + bc);
+        walk_emit(out, r + ar, c + ac);
+        return;
+    }
+    if (h == 2 && w == 3) { /* no 4-neighbour path joins these corners: one diagonal step */
+        walk_emit(out, r, c);
+        walk_emit(out, r + br, c + bc);
+        walk_emit(out, r + ar, c + ac);
+        walk_emit(out, r + ar + br, c + ac + bc);
+        walk_emit(out, r + 2 * ar + br, c + 2 * ac + bc);
+        walk_emit(out, r + 2 * ar, c + 2 * ac);
+        return;
+    }
+    if (h == 2 || w > 2 * h) { /* long block: two halves, both travelling along a */
+        const int64_t w1 = even_half(w);
+        walk(out, r, c, ar, ac, br, bc, w1, h);
+        walk(out, r + w1 * ar, c + w1 * ac, ar, ac, br, bc, w - w1, h);
+        return;
+    }
+    /* Four quadrants: near-left (travelling along b), far-left and far-right
+       (along a), near-right (back along -b, ending at the block's end corner).
+       Left widths and the near height are even where they can be, which keeps
+       every quadrant's own corners joinable by 4-neighbour steps. */
+    int64_t w1, h2;
+    if (w <= 3) {
+        w1 = w - 1;
+        h2 = 1;
+    } else {
+        w1 = even_half(w);
+        h2 = h / 2 < w / 2 ? h / 2 : w / 2;
+        if (h2 < 1) h2 = 1;
+    }
+    int64_t h1 = h - h2;
+    if (w > 3 && h1 % 2 == 1) {
+        if (h2 >= 2) {
+            h1 += 1;
+        } else {
+            h1 -= 1;
+        }
+    }
+    h2 = h - h1;
+    const int64_t w2 = w - w1;
+    walk(out, r, c, br, bc, ar, ac, h1, w1);
+    walk(out, r + h1 * br, c + h1 * bc, ar, ac, br, bc, w1, h2);
+    walk(out, r + w1 * ar + h1 * br, c + w1 * ac + h1 * bc, ar, ac, br, bc, w2, h2);
+    walk(out, r + (w - 1) * ar + (h1 - 1) * br, c + (w - 1) * ac + (h1 - 1) * bc, -br, -bc, -ar,
+         -ac, h1, w2);
+}
+
+int orc_hilbert_grid(int64_t rows, int64_t cols, int64_t* perm) {
+    if (rows < 1 || cols < 1) return -1;
+    walk_out out = {cols, perm, 0};
+    /* Start at (row 0, col 0), travel along the columns (a), turn down the rows
+       (b): as the classic curve. */
+    walk(&out, 0, 0, 0, 1, 1, 0, cols, rows);
+    return out.k == rows * cols ? 0 : -1;
+}
+
 int orc_order(const orc_spec* s, int64_t* perm) {
     const int64_t N = orc_num_tokens(s);
     if (s->order == ORC_ORDER_ROW_MAJOR) {
@@ -171,8 +278,8 @@ int orc_order(const orc_spec* s, int64_t* perm) {
         return 0;
     }
     if (s->order == ORC_ORDER_HILBERT) {
-        if (s->ndim != 2 || s->grid[0] != s->grid[1]) return -1;
-        return orc_hilbert(s->grid[0], perm);
+        if (s->ndim != 2) return -1;
+        return orc_hilbert_grid(s->grid[0], s->grid[1], perm);
     }
     if (s->order == ORC_ORDER_TILED) {
         const int64_t g0 = extent(s, 0), g1 = extent(s, 1), g2 = extent(s, 2);

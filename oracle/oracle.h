@@ -37,7 +37,7 @@ enum {
 enum {
     ORC_ORDER_ROW_MAJOR = 0,
     ORC_ORDER_TILED     = 1, /* tile by tile, row-major inside a tile */
-    ORC_ORDER_HILBERT   = 2  /* 2-D square power-of-two grid, Hilbert curve */
+    ORC_ORDER_HILBERT   = 2  /* 2-D grid, generalised Hilbert curve (orc_hilbert_grid) */
 };
 
 typedef struct {
@@ -49,6 +49,8 @@ typedef struct {
     int64_t dil;      /* ORC_WINDOW: dilation (1 = none) */
     int64_t tile;     /* ORC_STA: tile length */
     int64_t wt;       /* ORC_STA: window length in tiles */
+    int64_t shift;    /* ORC_WINDOW groups / ORC_BLOCKED windows start at positions
+                         congruent to -shift (0 <= shift < stride or w) */
 } orc_rule;
 
 typedef struct {
@@ -71,6 +73,15 @@ int orc_order(const orc_spec* s, int64_t* perm);
 /* Hilbert curve over an n x n grid (n a power of two), built by recursive
    quadrant subdivision.  perm[p] = row*n + col of the p-th cell. */
 int orc_hilbert(int64_t n, int64_t* perm);
+
+/* Generalised Hilbert curve over a rows x cols grid (any sizes >= 1): the
+   classic curve on power-of-two squares; otherwise the same quadrant U, or two
+   halves along the travel direction for blocks more than twice as long as
+   wide, split so that steps are 4-neighbour whenever the block's end corners
+   allow it (one diagonal step otherwise).  Starts at (0, 0); ends at
+   (0, cols - 1) when cols >= 2.  perm[p] = row*cols + col.  This is the order
+   of HILBERT specs. */
+int orc_hilbert_grid(int64_t rows, int64_t cols, int64_t* perm);
 
 /* Neighbourhood of the 1-D rule at coordinate x on an axis of length len.
    Writes the ascending list of positions to out (capacity len) and returns

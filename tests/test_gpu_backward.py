@@ -166,3 +166,9 @@ def test_backward_full_size(name):
     print("  sum dv vs sum dout: %.2e   |sum dk| / sqrt(sum |dk|^2): %.2e" % (e_dv, e_dk), flush=True)
     assert e_dv <= 1e-3
     assert e_dk <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["hwa96_bf16", "hswa96_bf16", "hna56_bf16", "hsa96_bf16"])
+def test_backward_hilbert_page(name):
+    """Gradients on the Hilbert page's shapes (generalised curve), two batches."""
+    _grad_case(W.scaled(W.HILBERT_PAGE[name], B=2))

@@ -281,3 +281,35 @@ def test_full_size(name, n_rows):
     wl = W.CONFIGS[name]
     rows = None if n_rows is None else _sample_rows(wl, n_rows, seed=wl["seed"])
     _run(wl, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# the Hilbert page's kernel-benchmark workloads (window, shifted window, slide
+# and neighbourhood attention on the curve; 56x56 and 96x96 on the generalised
+# curve): every element of every (batch, head), launched as the benchmark does
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(W.HILBERT_PAGE))
+def test_hilbert_page_full(name):
+    _run(W.HILBERT_PAGE[name])
+
+
+@pytest.mark.parametrize("name", ["hswa96_bf16", "hna56_bf16"])
+def test_hilbert_page_permute_passes(name):
+    _run(W.scaled(W.HILBERT_PAGE[name], B=2), permute_passes=True)
+
+
+@pytest.mark.parametrize("q_block", [192, 256])
+@pytest.mark.parametrize("name", ["hwa96_bf16", "hsa56_bf16"])
+def test_hilbert_page_query_blocks(name, q_block):
+    _run(W.scaled(W.HILBERT_PAGE[name], B=2), q_block=q_block)
+
+
+def test_hilbert_rectangular_grids():
+    """Non-square grids with odd sides (one diagonal step where the parity of
+    the sides forces it)."""
+    for grid, pat in (([37, 61], dict(kind="band", left=30, right=30)),
+                      ([45, 20], dict(kind="blocked", window=[48], shift=[24])),
+                      ([13, 100], dict(kind="na", window=[81]))):
+        _run(W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_%dx%d" % tuple(grid), B=1,
+                      H=2, grid=grid, pattern=pat))

@@ -99,6 +99,52 @@ def test_hilbert_invalid_side():
         oracle.hilbert(96)
 
 
+# The generalised curve (any rows x cols grid) is a reading: the pages name no
+# curve for the 56x56 and 96x96 inputs of the Hilbert page's Tables 1 and 3.
+# What pins it: it is the classic curve above on power-of-two squares, and on
+# every grid it has the properties that make it a Hilbert-type order.
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_hilbert_grid_reduces_to_classic(n):
+    assert np.array_equal(oracle.hilbert_grid(n, n), oracle.hilbert(n))
+
+
+def _four_neighbour_path_exists(rows, cols):
+    """Parity argument: colour cell (r, c) by (r + c) % 2.  A 4-neighbour path
+    alternates colours, so a path through all rows*cols cells from (0, 0) to
+    (0, cols-1) needs the two ends to differ in colour when rows*cols is even
+    (cols even) and to share the majority colour when it is odd (cols odd, rows
+    odd).  With one column the path simply runs down."""
+    return cols == 1 or cols % 2 == 0 or rows % 2 == 1
+
+
+@pytest.mark.parametrize("rows", list(range(1, 21)) + [56, 96])
+def test_hilbert_grid_properties(rows):
+    for cols in list(range(1, 21)) + [56, 96]:
+        perm = oracle.hilbert_grid(rows, cols)
+        assert sorted(perm.tolist()) == list(range(rows * cols)), (rows, cols)   # bijection
+        r, c = perm // cols, perm % cols
+        dr, dc = np.abs(np.diff(r)), np.abs(np.diff(c))
+        assert np.all(np.maximum(dr, dc) == 1), (rows, cols)    # every step to an adjacent cell
+        diagonal = int(np.sum((dr == 1) & (dc == 1)))
+        assert diagonal == (0 if _four_neighbour_path_exists(rows, cols) else 1), (rows, cols)
+        assert (r[0], c[0]) == (0, 0)
+        if cols >= 2:
+            assert (r[-1], c[-1]) == (0, cols - 1), (rows, cols)
+
+
+@pytest.mark.parametrize("rows,cols", [(96, 96), (56, 56), (100, 60), (30, 200), (97, 61)])
+def test_hilbert_grid_locality(rows, cols):
+    """Every run of L consecutive cells lies in a bounding box of at most 3L cells
+    (the classic curve on 128 x 128 stays under 2L for these L)."""
+    perm = oracle.hilbert_grid(rows, cols)
+    r, c = perm // cols, perm % cols
+    for L in (16, 49, 64):
+        for s in range(0, rows * cols - L + 1, 3):
+            rr, cc = r[s:s + L], c[s:s + L]
+            assert (np.ptp(rr) + 1) * (np.ptp(cc) + 1) <= 3 * L, (rows, cols, L, s)
+
+
 # ---------------------------------------------------------------------------
 # 1-D rules against brute force
 # ---------------------------------------------------------------------------
@@ -145,6 +191,51 @@ def test_rule_blocked(L):
             # blocked == window of w with stride w, cut at the ends
             strided = oracle.rule_set(dict(kind="sa", window=[w], stride=[w]), 0, L, x).tolist()
             assert strided == got, (L, w, x)
+
+
+def bf_shifted_blocked(L, w, shift, x):
+    """Windows [k*w - shift, (k+1)*w - shift) as a partition: same window index."""
+    return [j for j in range(L) if (j + shift) // w == (x + shift) // w]
+
+
+def cyclic_shift_windows(L, w, s):
+    """Shifted windows built the way Swin builds them: roll the sequence back by s,
+    cut windows of w, and mask pairs whose tokens came from different segments
+    of the unrolled sequence (the wrapped tail).  Returns the key sets per
+    query.  L must be a multiple of w."""
+    rolled = [(p + s) % L for p in range(L)]          # rolled slot t holds token rolled[t]
+    label = [0 if t < L - s else 1 for t in range(L)]  # wrapped tokens form their own segment
+    keys = {x: [] for x in range(L)}
+    for t in range(L):
+        for u in range(L):
+            if t // w == u // w and label[t] == label[u]:
+                keys[rolled[t]].append(rolled[u])
+    return {x: sorted(v) for x, v in keys.items()}
+
+
+@pytest.mark.parametrize("L", [1, 4, 10, 17, 24])
+def test_rule_shifted_blocked(L):
+    for w in [1, 2, 3, 4, 8]:
+        for shift in range(w):
+            pat = dict(kind="blocked", window=[w], shift=[shift])
+            for x in range(L):
+                got = oracle.rule_set(pat, 0, L, x).tolist()
+                assert got == bf_shifted_blocked(L, w, shift, x), (L, w, shift, x)
+                # the same windows as a window of w with stride w and shifted groups
+                strided = oracle.rule_set(dict(kind="sa", window=[w], stride=[w], shift=[shift]),
+                                          0, L, x).tolist()
+                assert strided == got, (L, w, shift, x)
+
+
+@pytest.mark.parametrize("L,w", [(16, 4), (24, 8), (64, 16), (30, 6)])
+def test_shifted_windows_equal_cyclic_shift_with_mask(L, w):
+    """Shift s by roll-and-mask equals truncated windows whose boundaries sit at
+    positions congruent to s (phase w - s); at s = w / 2 the two phases agree."""
+    for s in range(1, w):
+        ref = cyclic_shift_windows(L, w, s)
+        pat = dict(kind="blocked", window=[w], shift=[w - s])
+        for x in range(L):
+            assert oracle.rule_set(pat, 0, L, x).tolist() == ref[x], (L, w, s, x)
 
 
 @pytest.mark.parametrize("L,tile,wt", [(30, 6, 3), (48, 8, 5), (80, 8, 7), (10, 4, 1),

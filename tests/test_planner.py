@@ -100,16 +100,20 @@ def _random_workload(rng):
         left, right = int(rng.integers(0, 40)), int(rng.integers(0, 40))
         return dict(grid=[n], pattern=dict(kind="band", left=left, right=right))
     if kind == "hilbert":
-        n = int(2 ** rng.integers(1, 5))
+        if rng.random() < 0.3:
+            grid = [int(2 ** rng.integers(1, 5))] * 2
+        else:
+            grid = [int(rng.integers(1, 14)), int(rng.integers(1, 14))]
         sub = rng.choice(["band", "blocked", "na"])
         if sub == "band":
             r = int(rng.integers(0, 20))
             pat = dict(kind="band", left=r, right=int(rng.integers(0, 20)))
         elif sub == "blocked":
-            pat = dict(kind="blocked", window=[int(rng.integers(1, 20))])
+            w = int(rng.integers(1, 20))
+            pat = dict(kind="blocked", window=[w], shift=[int(rng.integers(0, w))])
         else:
             pat = dict(kind="na", window=[int(rng.integers(1, 30))])
-        return dict(grid=[n, n], order="hilbert", pattern=pat)
+        return dict(grid=grid, order="hilbert", pattern=pat)
     ndim = int(rng.integers(1, 4))
     grid = [int(rng.integers(1, 12)) for _ in range(ndim)]
     if kind == "sta":
@@ -123,7 +127,10 @@ def _random_workload(rng):
     pat = dict(kind=kind, window=window)
     if kind in ("na", "sa"):
         pat["stride"] = [int(rng.integers(1, min(3, w) + 1)) for w in window]
+        pat["shift"] = [int(rng.integers(0, st)) for st in pat["stride"]]
         pat["dilation"] = [int(rng.integers(1, 3)) for _ in grid]
+    if kind == "blocked":
+        pat["shift"] = [int(rng.integers(0, w)) for w in window]
     wl = dict(grid=grid, pattern=pat)
     if rng.random() < 0.3:
         wl["order"] = "tiled"
@@ -144,19 +151,29 @@ def test_random_tiny_workloads():
             raise AssertionError("workload %r qb=%d kb=%d: %s" % (wl, qb, kb, e))
 
 
-def test_hilbert_non_power_of_two_unsupported():
-    wl = dict(grid=[96, 96], order="hilbert", pattern=dict(kind="band", left=5, right=5),
-              D=64, dtype="bf16")
-    with pytest.raises(na.NaError) as ei:
-        na.Plan(wl, host_only=True)
-    assert ei.value.status == na.NA_ERR_UNSUPPORTED
+@pytest.mark.parametrize("rows", list(range(1, 26)) + [56, 96])
+def test_hilbert_order_any_grid_matches_oracle(rows):
+    for cols in list(range(1, 26)) + [56, 96]:
+        wl = dict(grid=[rows, cols], order="hilbert", pattern=dict(kind="band", left=1, right=1))
+        p = _plan(wl, 16, 16)
+        assert np.array_equal(p.order().astype(np.int64), oracle.hilbert_grid(rows, cols)), \
+            (rows, cols)
+
+
+def test_hilbert_needs_2d_grid():
+    for grid in ([64], [4, 4, 4]):
+        wl = dict(grid=grid, order="hilbert", pattern=dict(kind="band", left=5, right=5),
+                  D=64, dtype="bf16")
+        with pytest.raises(na.NaError) as ei:
+            na.Plan(wl, host_only=True)
+        assert ei.value.status == na.NA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("field,value", [
     ("ndim", 0), ("ndim", 4), ("grid", [0, 4, 1]), ("order", 7), ("dtype", 9), ("head_dim", 0),
     ("window", [0, 3, 1]), ("stride", [3, 0, 1]), ("dilation", [1, 0, 1]), ("causal", [2, 0, 0]),
     ("boundary", [5, 0, 0]), ("window_left", [-3, -1, -1]), ("q_block", -1), ("kv_block", -5),
-    ("stride", [4, 1, 1]),
+    ("stride", [4, 1, 1]), ("shift", [1, 0, 0]), ("shift", [-1, 0, 0]),
 ])
 def test_invalid_descriptors(field, value):
     d = na.desc_from_workload(dict(grid=[4, 4], pattern=dict(kind="na", window=[3, 3]), D=64,
@@ -197,3 +214,13 @@ def test_host_only_plan_cannot_run():
     st = na.lib().na_forward(p._h, 1, 1, t, t, t, t, None, 0.1, 0, None, 0, None)
     assert st == na.NA_ERR_PLAN_MISMATCH
     del torch
+
+
+def test_hilbert_page_workloads_reproduce_printed_sparsity():
+    """At the page's block size (128 x 128) the workloads built for the Hilbert
+    page's Tables 1-3 have the empty-block ratios printed there: HWA 96x96 8x8
+    98.61 %, HWA 128x128 16x16 98.44 %, HSA 96x96 95.87 %."""
+    printed = {"hwa96_bf16": 98.61, "hwa128_bf16": 98.44, "hsa96_bf16": 95.87}
+    for name, pct in printed.items():
+        st = na.Plan(W.HILBERT_PAGE[name], host_only=True, q_block=128, kv_block=128).stats
+        assert round(100.0 * st["n_empty"] / (st["n_q_tiles"] * st["n_kv_tiles"]), 2) == pct, name
