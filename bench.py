@@ -103,6 +103,10 @@ def main():
                     help="time the forward (default) or the backward pass (dq, dk, dv from the "
                          "forward's out and lse; effective flops 10 * D per attended pair: the "
                          "recomputed score and the dP, dV, dK, dQ products)")
+    ap.add_argument("--vs-dense", action="store_true",
+                    help="also time dense attention of the same shape on the same kernel (window "
+                         "= whole grid) and report the measured speedup beside the tile map's "
+                         "speedup bounds")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the row-permute kernel over 268,435,456 bytes (read once, "
                          "written once): the known-size copy that calibrates HBM counters")
@@ -187,6 +191,38 @@ def main():
     hbm_bound = alg_bytes / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
 
+    sparsity = None
+    if args.vs_dense:
+        if args.which != "forward" or args.permute_passes:
+            raise SystemExit("--vs-dense times the plain forward pass only")
+        n_tok = plan.n_tokens
+        if wl["order"] == "hilbert":
+            dense_pat = dict(kind="band", left=n_tok, right=n_tok)
+        else:
+            dense_pat = dict(kind="na", window=list(wl["grid"]))
+        dense = na.Plan(W.scaled(wl, pattern=dense_pat), q_block=args.q_block)
+        dense_out = torch.empty_like(q)
+        dense_lse = torch.empty_like(lse)
+
+        def dense_step():
+            dense.forward(q, k, v, out=dense_out, lse=dense_lse, scale=scale)
+
+        dense_steps = max(2, args.steps // 4)
+        for _ in range(2):
+            dense_step()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(dense_steps):
+            dense_step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = start.elapsed_time(end) / dense_steps
+        log("bench: dense %.3f ms/step" % dense_ms)
+        sparsity = {"dense_ms_per_step": round(dense_ms, 4),
+                    "dense_tflops": round(dense.effective_flops(B, H) / (dense_ms * 1e-3) / 1e12, 3),
+                    "speedup_vs_dense": round(dense_ms / ms, 4),
+                    "bounds": {k: round(x, 4) for k, x in plan.speedup_bounds().items()}}
+
     cpu = None
     if not args.no_cpu_baseline and args.which == "forward":
         log("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
@@ -229,6 +265,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if sparsity is not None:
+        line["sparsity"] = sparsity
     print(json.dumps(line), flush=True)
 
 

@@ -741,7 +741,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(NaAttnParams p) {
 bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block) {
     if (dtype == NA_BF16)
         return (head_dim == 64 || head_dim == 128) && kv_block == NA_KV_BLOCK_BF16 &&
-               (q_block == 128 || q_block == 192 || q_block == 256);
+               (q_block == 128 || q_block == 192 || q_block == 256 ||
+                (q_block == 64 && head_dim == 64));
     if (dtype == NA_F32)
         return (head_dim == 32 || head_dim == 64) && kv_block == NA_KV_BLOCK_F32 &&
                q_block == NA_Q_BLOCK_F32;
@@ -752,7 +753,9 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
     hipStream_t st = (hipStream_t)stream;
     const dim3 grid((unsigned)p.n_wg);
     if (dtype == NA_BF16) {
-        if (head_dim == 128 && q_block == 128)
+        if (head_dim == 64 && q_block == 64)
+            hipLaunchKernelGGL((attn_fwd_bf16<64, 2>), grid, dim3(128), 0, st, p);
+        else if (head_dim == 128 && q_block == 128)
             hipLaunchKernelGGL((attn_fwd_bf16<128, 4>), grid, dim3(256), 0, st, p);
         else if (head_dim == 128 && q_block == 256)
             hipLaunchKernelGGL((attn_fwd_bf16<128, 8>), grid, dim3(512), 0, st, p);

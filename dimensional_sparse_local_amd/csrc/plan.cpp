@@ -110,6 +110,7 @@ struct Axis {
     int64_t L, w, left, stride, dil;
     bool clamp;
     int64_t shift;  // stride-group phase
+    bool causal;    // leader = last position of its group (block-causal groups)
 };
 
 // [lo, hi) of the keys of coordinate x on one axis, in axis coordinates; with
@@ -118,7 +119,8 @@ void axis_window(const Axis& a, int64_t x, int32_t* lo, int32_t* hi) {
     const int64_t g = x % a.dil;
     const int64_t xl = x / a.dil;
     const int64_t Lg = ceil_div(a.L - g, a.dil);
-    const int64_t c = ((xl + a.shift) / a.stride) * a.stride - a.shift + a.stride / 2;
+    const int64_t first = ((xl + a.shift) / a.stride) * a.stride - a.shift;
+    const int64_t c = first + (a.causal ? a.stride - 1 : a.stride / 2);
     int64_t s, e;
     if (a.clamp) {
         if (a.w >= Lg) {
@@ -211,7 +213,7 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
     Axis ax[3];
     for (int i = 0; i < 3; ++i) {
         if (i >= pdims) {
-            ax[i] = Axis{1, 1, 0, 1, 1, true, 0};
+            ax[i] = Axis{1, 1, 0, 1, 1, true, 0, false};
             p->plen[i] = 1;
             p->left[i] = 0;
             p->clamp[i] = 1;
@@ -260,7 +262,7 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
         }
         d.window_left[i] = (int32_t)left;
         ax[i] = Axis{L, d.window[i], left, d.stride[i], d.dilation[i],
-                     d.boundary[i] == NA_BOUND_CLAMP, d.shift[i]};
+                     d.boundary[i] == NA_BOUND_CLAMP, d.shift[i], d.causal[i] != 0};
         p->plen[i] = (int32_t)L;
         p->left[i] = (int32_t)left;
         p->clamp[i] = d.boundary[i] == NA_BOUND_CLAMP;

@@ -131,6 +131,7 @@ def desc_from_workload(w: dict, q_block: int = 0, kv_block: int = 0) -> Desc:
             d.stride[i] = int(pat.get("stride", [1, 1, 1])[i])
             d.shift[i] = int(pat.get("shift", [0, 0, 0])[i])
             d.dilation[i] = int(pat.get("dilation", [1, 1, 1])[i])
+            d.causal[i] = int(pat.get("causal", [0, 0, 0])[i])
             d.boundary[i] = NA_BOUND_CLAMP if kind == "na" else NA_BOUND_TRUNCATE
         elif kind == "band":
             left, right = int(pat["left"]), int(pat["right"])
@@ -210,6 +211,31 @@ class Plan:
     def effective_flops(self, B: int, H: int) -> int:
         """Unmasked QK^T + PV flops: 4 * D * attended pairs * B * H."""
         return 4 * self.head_dim * self.stats["attended_pairs"] * B * H
+
+    def speedup_bounds(self) -> dict:
+        """Upper bounds on the speedup of this pattern over dense attention of
+        the same length and tile sizes, from the tile map alone (the kind of
+        bound the "Generalized Neighborhood Attention" page's simulator gives,
+        abstract: realistic rather than flop-count bounds):
+
+        * ``flop``: N^2 / attended pairs, what counting flops promises;
+        * ``tile``: dense tile pairs / non-empty tile pairs, what a kernel that
+          skips empty tiles and pays full price for every other tile can reach;
+        * ``useful_fraction``: attended pairs / pairs inside non-empty tiles
+          (1.0 when every visited tile is full: a perfectly block-sparse map).
+        """
+        st = self.stats
+        n = st["n_tokens"]
+        visited = st["n_partial"] + st["n_full"]
+        pairs = st["attended_pairs"]
+        # pairs inside the visited tiles, with the ragged last tiles at their true size
+        q_sizes = np.minimum(st["q_block"], n - np.arange(st["n_q_tiles"]) * st["q_block"])
+        k_sizes = np.minimum(st["kv_block"], n - np.arange(st["n_kv_tiles"]) * st["kv_block"])
+        visited_rows = self.classes() != 0
+        inside = int(np.sum(q_sizes * (visited_rows @ k_sizes.astype(np.int64))))
+        return {"flop": n * n / pairs if pairs else float("inf"),
+                "tile": st["n_q_tiles"] * st["n_kv_tiles"] / visited if visited else float("inf"),
+                "useful_fraction": pairs / inside if inside else 1.0}
 
     # -- device calls --------------------------------------------------------
 

@@ -9,8 +9,9 @@ Pattern vocabulary (per grid dimension unless noted):
 * ``na``      window of ``window[d]`` positions centred on the query and shifted
               inside the grid at the borders (neighbourhood attention);
               optional ``stride`` (groups sharing one window), ``shift`` (the
-              groups' phase: they start at positions congruent to -shift) and
-              ``dilation``.
+              groups' phase: they start at positions congruent to -shift),
+              ``dilation`` and ``causal`` (per dimension: the window ends at
+              the query and is cut at the start, e.g. causal in time for video).
 * ``sa``      the same window cut at the grid borders instead of shifted
               (slide attention, zero padding).
 * ``band``    1-D only: keys in [x - left, x + right] cut at the ends
@@ -91,8 +92,30 @@ HILBERT_PAGE = {
         note="Hilbert neighbourhood attention, 96x96 input, 7x7 kernel (Table 3)"),
 }
 
+# Generalised neighbourhood attention beyond the five benchmark shapes
+# ("Generalized Neighborhood Attention", abstract: sliding, strided and blocked
+# windows in any number of dimensions).
+GNA = {
+    # the 64x64 13x13 neighbourhood workload with the token order cut into 8x8
+    # patches: same neighbourhoods, fewer and denser tile pairs
+    "na2d_tiled_bf16": dict(
+        name="na2d_tiled_bf16", B=2, H=8, D=64, dtype="bf16", grid=[64, 64], order="tiled",
+        tile=[8, 8], pattern=dict(kind="na", window=[13, 13]), seed=21,
+        note="2-D neighbourhood attention, 64x64 grid, 13x13 window, 8x8 patch order"),
+    # sliding tile attention on the 30x48x80 video grid made causal in time:
+    # each chunk of 6 frames attends to itself and the chunk before it, and to
+    # the 3x5 spatial tiles around its own (block-causal video attention)
+    "sta3d_causal_t_bf16": dict(
+        name="sta3d_causal_t_bf16", B=1, H=24, D=128, dtype="bf16", grid=[30, 48, 80],
+        order="tiled", tile=[6, 8, 8],
+        pattern=dict(kind="na", window=[12, 24, 40], stride=[6, 8, 8], causal=[1, 0, 0]),
+        seed=22,
+        note="3-D sliding tile attention causal in time, 30x48x80 grid, 6x8x8 tiles, "
+             "2 chunks of 6 frames x 3x5 tiles"),
+}
+
 # Every named workload.
-ALL = {**CONFIGS, **HILBERT_PAGE}
+ALL = {**CONFIGS, **HILBERT_PAGE, **GNA}
 
 # The workload the benchmark times by default (the headline metric's config).
 HEADLINE = "sta3d_bf16"

@@ -98,14 +98,17 @@ enum { NA_BF16 = 0, NA_F32 = 1 };
  * NA_ORDER_HILBERT where there is one pattern dimension: the curve position,
  * of length N.  For pattern dimension d with length L, a query at coordinate x
  * attends the keys y with
- *     c   = ((x' + shift) / stride) * stride - shift + stride / 2   (x' = x / dilation)
+ *     c   = ((x' + shift) / stride) * stride - shift + stride / 2   (x' = x / dilation;
+ *                                        the group's last position, + stride - 1, when causal)
  *     lo  = c - left, hi = lo + window                 (left = window_left, or window / 2,
  *                                                       or window - 1 when causal)
  *     clamp:    [lo, hi) shifted to lie inside [0, L'), or all of [0, L') if window >= L'
  *     truncate: [lo, hi) cut to [0, L')
  * evaluated on the sub-grid of positions congruent to x modulo dilation (L' its length), and
  * the N-D set is the Cartesian product of the per-dimension sets.  A causal dimension uses
- * left = window - 1 and truncation.
+ * left = window - 1 and truncation, and its stride groups are led by their last position, so a
+ * group of `stride` positions (a chunk of frames, say) attends to itself and the window - stride
+ * positions before it (block-causal); with stride 1 this is plain causal attention.
  */
 typedef struct {
     int32_t ndim;           /* grid dimensions, 1..3 */
@@ -177,7 +180,8 @@ size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t
  * Returns NA_ERR_PLAN_MISMATCH if the plan was built host-only, and
  * NA_ERR_UNSUPPORTED if no kernel matches (dtype, head_dim, q_block,
  * kv_block): bf16 with head_dim 64 or 128 and (q_block, kv_block) =
- * (128, 64), (192, 64) or (256, 64); fp32 with head_dim 32 or 64 and (32, 32).
+ * (128, 64), (192, 64) or (256, 64), and (64, 64) at head_dim 64; fp32 with head_dim 32 or
+ * 64 and (32, 32).
  * In bf16 the probabilities are rounded to bf16 before they enter both P.V and
  * the row sum, so lse carries a relative row-sum error of at most 2^-8. */
 na_status na_forward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,

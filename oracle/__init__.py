@@ -45,6 +45,7 @@ class _Rule(ctypes.Structure):
         ("tile", ctypes.c_int64),
         ("wt", ctypes.c_int64),
         ("shift", ctypes.c_int64),
+        ("causal", ctypes.c_int64),
     ]
 
 
@@ -133,6 +134,9 @@ def _rule_for(pattern: dict, d: int) -> _Rule:
         r.stride = int(pattern.get("stride", [1, 1, 1])[d])
         r.dil = int(pattern.get("dilation", [1, 1, 1])[d])
         r.shift = int(pattern.get("shift", [0, 0, 0])[d])
+        if int(pattern.get("causal", [0, 0, 0])[d]):
+            # causal dimension: the w positions ending at the query, cut at the start
+            r.left, r.clamp, r.causal = w - 1, 0, 1
     elif kind == "band":
         left, right = int(pattern["left"]), int(pattern["right"])
         r.kind, r.clamp, r.w, r.left = ORC_WINDOW, 0, left + right + 1, left

@@ -65,7 +65,8 @@ static int64_t extent(const orc_spec* s, int d) { return d < s->ndim ? s->grid[d
    neighbourhood-attention border rule); without it the window is cut at the
    axis ends (positions outside are invalid and dropped).  Stride: positions are
    grouped `stride` at a time (groups start at positions congruent to -shift)
-   and each group uses the window of its middle position.  Dilation: only positions congruent to x modulo `dil` take part,
+   and each group uses the window of its middle position (of its last position
+   for a causal rule, whose window ends there).  Dilation: only positions congruent to x modulo `dil` take part,
    and the rule runs in the coordinates of that sub-grid. */
 static int64_t window_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out) {
     const int64_t dil = r->dil > 0 ? r->dil : 1;
@@ -75,7 +76,9 @@ static int64_t window_set(const orc_rule* r, int64_t L, int64_t x, int64_t* out)
     const int64_t Lg = ceil_div(L - g, dil);   /* its length */
     /* group leader; with stride 1 every position leads its own group */
     const int64_t first = ((xl + r->shift) / stride) * stride - r->shift; /* group start */
-    const int64_t centre = first + stride / 2;
+    /* the middle position leads its group; a causal group is led by its last
+       position, so every member sees the whole group */
+    const int64_t centre = first + (r->causal ? stride - 1 : stride / 2);
     int64_t lo, hi;
     if (r->clamp) {
         if (r->w >= Lg) {

@@ -51,6 +51,8 @@ typedef struct {
     int64_t wt;       /* ORC_STA: window length in tiles */
     int64_t shift;    /* ORC_WINDOW groups / ORC_BLOCKED windows start at positions
                          congruent to -shift (0 <= shift < stride or w) */
+    int64_t causal;   /* ORC_WINDOW: 1 = the window ends at the group's last position
+                         (set with left = w - 1 and clamp = 0) */
 } orc_rule;
 
 typedef struct {

@@ -172,3 +172,20 @@ def test_backward_full_size(name):
 def test_backward_hilbert_page(name):
     """Gradients on the Hilbert page's shapes (generalised curve), two batches."""
     _grad_case(W.scaled(W.HILBERT_PAGE[name], B=2))
+
+
+GNA = [
+    W.scaled(W.CONFIGS["na2d_bf16"], name="na3d_causal_t", B=1, H=2, grid=[8, 12, 10],
+             pattern=dict(kind="na", window=[3, 5, 5], causal=[1, 0, 0])),
+    W.scaled(W.GNA["sta3d_causal_t_bf16"], name="block_causal_small", H=2, grid=[18, 16, 24],
+             pattern=dict(kind="na", window=[12, 16, 24], stride=[6, 8, 8], causal=[1, 0, 0])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="stride_shift_2d", B=1, H=2, grid=[20, 30],
+             pattern=dict(kind="na", window=[7, 9], stride=[3, 3], shift=[1, 2])),
+    W.GNA["na2d_tiled_bf16"],
+]
+
+
+@pytest.mark.parametrize("q_block", [128, 256])
+@pytest.mark.parametrize("wl", GNA, ids=[w["name"] for w in GNA])
+def test_backward_gna(wl, q_block):
+    _grad_case(wl, q_block=q_block)

@@ -313,3 +313,45 @@ def test_hilbert_rectangular_grids():
                       ([13, 100], dict(kind="na", window=[81]))):
         _run(W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_%dx%d" % tuple(grid), B=1,
                       H=2, grid=grid, pattern=pat))
+
+
+# ---------------------------------------------------------------------------
+# generalised neighbourhood attention: causal in time (plain and block-causal),
+# shifted stride groups, patch token orders
+# ---------------------------------------------------------------------------
+
+GNA_SMALL = [
+    W.scaled(W.CONFIGS["na2d_bf16"], name="na3d_causal_t", B=1, H=2, grid=[8, 12, 10],
+             pattern=dict(kind="na", window=[3, 5, 5], causal=[1, 0, 0])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="na3d_causal_t_tiled", B=1, H=2, grid=[8, 12, 10],
+             order="tiled", tile=[2, 4, 5],
+             pattern=dict(kind="na", window=[3, 5, 5], causal=[1, 0, 0])),
+    W.scaled(W.GNA["sta3d_causal_t_bf16"], name="block_causal_small", H=2, grid=[18, 16, 24],
+             pattern=dict(kind="na", window=[12, 16, 24], stride=[6, 8, 8], causal=[1, 0, 0])),
+    W.scaled(W.CONFIGS["na2d_bf16"], name="stride_shift_2d", B=1, H=2, grid=[20, 30],
+             pattern=dict(kind="na", window=[7, 9], stride=[3, 3], shift=[1, 2])),
+    W.scaled(W.CONFIGS["causal1d_bf16"], name="block_causal_1d", H=2, grid=[1000],
+             pattern=dict(kind="na", window=[256], stride=[64], causal=[1])),
+    W.GNA["na2d_tiled_bf16"],
+]
+
+
+@pytest.mark.parametrize("wl", GNA_SMALL, ids=[w["name"] for w in GNA_SMALL])
+def test_gna_small(wl):
+    _run(wl)
+
+
+def test_block_causal_video_full_size():
+    wl = W.GNA["sta3d_causal_t_bf16"]
+    _run(wl, rows=_sample_rows(wl, 24, seed=wl["seed"]))
+
+
+# 64-query tiles (head_dim 64): one tile per 64-position window of HWA
+Q64 = [w for w in SMALL_BF16 if w["D"] == 64] + [
+    W.scaled(W.HILBERT_PAGE["hwa96_bf16"], B=2), W.scaled(W.HILBERT_PAGE["hna56_bf16"], B=2),
+    W.GNA["na2d_tiled_bf16"]]
+
+
+@pytest.mark.parametrize("wl", Q64, ids=[w["name"] for w in Q64])
+def test_query_block_64(wl):
+    _run(wl, q_block=64)

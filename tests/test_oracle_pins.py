@@ -272,6 +272,42 @@ def test_rule_stride_and_dilation(L):
                         assert got == want, (kind, L, w, s, dil, x)
 
 
+def bf_causal(L, w, stride, x):
+    """Causal window of w positions as a filter: the keys j with
+    0 <= last - j < w, where `last` is the final position of x's group of
+    `stride` (block-causal: a chunk sees itself and the w - stride positions
+    before it; stride 1 is Eq. 5 of the pi-Attention page with k = w - 1)."""
+    last = (x // stride) * stride + stride - 1
+    return [j for j in range(L) if 0 <= last - j < w]
+
+
+@pytest.mark.parametrize("L", [1, 6, 13])
+def test_rule_causal(L):
+    for w in [1, 2, 3, 5, 8]:
+        for s in range(1, w + 1):
+            for x in range(L):
+                got = oracle.rule_set(dict(kind="na", window=[w], stride=[s], causal=[1]), 0, L,
+                                      x).tolist()
+                assert got == bf_causal(L, w, s, x), (L, w, s, x)
+                assert x in got  # every position sees itself
+                if s == 1:
+                    band = oracle.rule_set(dict(kind="band", left=w - 1, right=0), 0, L, x)
+                    assert got == band.tolist()
+
+
+def test_neighbors_nd_causal_in_time():
+    """Video-style 3-D window: causal in time (first axis), neighbourhood in
+    space, as the product of the per-axis sets."""
+    wl = dict(grid=[6, 5, 7], pattern=dict(kind="na", window=[3, 3, 5], causal=[1, 0, 0]))
+    for i in range(0, 210, 7):
+        c0, c1, c2 = i // 35, (i // 7) % 5, i % 7
+        want = sorted((a * 5 + b) * 7 + c
+                      for a in bf_causal(6, 3, 1, c0)
+                      for b in bf_window_clamp(5, 3, c1)
+                      for c in bf_window_clamp(7, 5, c2))
+        assert oracle.neighbors(wl, i).tolist() == want
+
+
 def test_neighbors_nd_is_product():
     wl = dict(grid=[5, 6, 7], pattern=dict(kind="na", window=[3, 5, 3]))
     for i in [0, 17, 100, 209]:

@@ -129,6 +129,7 @@ def _random_workload(rng):
         pat["stride"] = [int(rng.integers(1, min(3, w) + 1)) for w in window]
         pat["shift"] = [int(rng.integers(0, st)) for st in pat["stride"]]
         pat["dilation"] = [int(rng.integers(1, 3)) for _ in grid]
+        pat["causal"] = [int(rng.random() < 0.3) for _ in grid]
     if kind == "blocked":
         pat["shift"] = [int(rng.integers(0, w)) for w in window]
     wl = dict(grid=grid, pattern=pat)
@@ -224,3 +225,45 @@ def test_hilbert_page_workloads_reproduce_printed_sparsity():
     for name, pct in printed.items():
         st = na.Plan(W.HILBERT_PAGE[name], host_only=True, q_block=128, kv_block=128).stats
         assert round(100.0 * st["n_empty"] / (st["n_q_tiles"] * st["n_kv_tiles"]), 2) == pct, name
+
+
+def test_block_causal_video_closed_form():
+    """STA causal in time: the first 6-frame chunk sees 6 frames, the other
+    four see 12; in space every query sees 3x5 whole 8x8 tiles (24 x 40,
+    shifted inside).  Pairs per head = 3840 * (6 * 6 * 960 + 24 * 12 * 960)."""
+    wl = W.GNA["sta3d_causal_t_bf16"]
+    st = na.Plan(wl, host_only=True, q_block=128, kv_block=64).stats
+    assert st["attended_pairs"] == 48 * 80 * (6 * 6 * 960 + 24 * 12 * 960) == 1194393600
+    # tile-aligned: every visited tile pair is full (a query tile lies in one
+    # 384-token tile whose key tiles are all attended or all not)
+    assert st["n_partial"] == 0
+    # per query tile: chunk 0 attends 1 chunk, the others 2, each of 15 spatial tiles
+    # of 6 key tiles (64 keys) per 384-token tile
+    assert st["n_full"] == 3 * 60 * (1 * 15 * 6) + 3 * 240 * (2 * 15 * 6)
+
+
+def test_patch_order_same_neighbourhoods_denser_tiles():
+    """8x8 patch order for the 64x64 13x13 neighbourhood workload: identical
+    neighbourhoods (pairs), 308 instead of 442 visited tile pairs."""
+    a = na.Plan(W.CONFIGS["na2d_bf16"], host_only=True, q_block=128, kv_block=64)
+    b = na.Plan(W.GNA["na2d_tiled_bf16"], host_only=True, q_block=128, kv_block=64)
+    assert a.stats["attended_pairs"] == b.stats["attended_pairs"] == 692224
+    assert a.stats["n_partial"] + a.stats["n_full"] == 442
+    assert b.stats["n_partial"] + b.stats["n_full"] == 308
+
+
+def test_speedup_bounds():
+    # perfectly block-sparse: the tile bound equals the flop bound, 115200 / 40320
+    sb = na.Plan(W.CONFIGS["sta3d_bf16"], host_only=True, q_block=128).speedup_bounds()
+    assert sb["flop"] == pytest.approx(115200 / 40320) and sb["tile"] == pytest.approx(300 / 105)
+    assert sb["useful_fraction"] == 1.0
+    # row-major neighbourhood attention: flop bound 4096^2 / 692224, tile bound
+    # 32 * 64 / 442; useful fraction 692224 / (442 * 128 * 64)
+    sb = na.Plan(W.CONFIGS["na2d_bf16"], host_only=True, q_block=128).speedup_bounds()
+    assert sb["flop"] == pytest.approx(4096 ** 2 / 692224)
+    assert sb["tile"] == pytest.approx(2048 / 442)
+    assert sb["useful_fraction"] == pytest.approx(692224 / (442 * 128 * 64))
+    # ragged tiles count at their true size: a dense 100-token window
+    sb = na.Plan(dict(grid=[100], pattern=dict(kind="band", left=100, right=100), D=64,
+                      dtype="bf16"), host_only=True, q_block=128).speedup_bounds()
+    assert sb == {"flop": 1.0, "tile": 1.0, "useful_fraction": 1.0}
