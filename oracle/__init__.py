@@ -56,7 +56,14 @@ class _Spec(ctypes.Structure):
         ("order", ctypes.c_int32),
         ("tile", ctypes.c_int64 * 3),
         ("rule", _Rule * 3),
+        ("skip", ctypes.c_int64),
+        ("skip_both", ctypes.c_int32),
+        ("skip_mode", ctypes.c_int32),
+        ("skip_prior", ctypes.c_double),
     ]
+
+
+SKIP_MODES = {"union": 0, "fixed_fusion": 1, "separate": 2}
 
 
 def build(force: bool = False) -> str:
@@ -170,6 +177,13 @@ def spec(workload: dict) -> _Spec:
     else:
         for d in range(len(grid)):
             s.rule[d] = _rule_for(pat, d)
+    # pi-Attention's online partner (1-D patterns only)
+    s.skip = int(pat.get("skip", 0))
+    if s.skip and order != "hilbert" and len(grid) != 1:
+        raise ValueError("the skip partner needs a 1-D pattern (1-D grid or Hilbert order)")
+    s.skip_both = int(pat.get("skip_both", 0))
+    s.skip_mode = SKIP_MODES[pat.get("skip_mode", "union")]
+    s.skip_prior = float(pat.get("skip_prior", 0.5))
     return s
 
 

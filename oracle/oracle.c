@@ -20,6 +20,12 @@
  *    readings (the pages give only the names): a group of `stride` consecutive
  *    positions shares the window of its middle position; dilation runs the
  *    rule on the interleaved sub-grid of positions congruent to x.
+ *  - pi-Attention's online long-range partner (pi-Attention, Section 3.4,
+ *    Eqs. 8-11) and its fusion variants (Section 3.5: separate softmax,
+ *    Eq. 15; fixed fusion, Eqs. 16-17).  The output of the separate variant
+ *    is a reading: the page defines the two branch softmaxes only, and the
+ *    output is taken as Eq. 11 with those weights (the two weighted averages
+ *    added).
  *  - Hilbert reordering with windows / slides formed on the reordered 1-D
  *    sequence, and the empty / partial / full tile classes:
  *    "Hilbert-Guided Sparse Local Attention", "Methodology in Plain English"
@@ -312,8 +318,9 @@ static int cmp_i64(const void* a, const void* b) {
     return (x > y) - (x < y);
 }
 
-int64_t orc_neighbors(const orc_spec* s, const int64_t* perm, const int64_t* pos_of_token,
-                      int64_t i, int64_t* out) {
+/* The local set N_r(i): the pattern's neighbourhood. */
+static int64_t local_neighbors(const orc_spec* s, const int64_t* perm,
+                               const int64_t* pos_of_token, int64_t i, int64_t* out) {
     const int64_t N = orc_num_tokens(s);
     if (s->order == ORC_ORDER_HILBERT) {
         /* The rule acts on positions along the curve; keys are mapped back to
@@ -349,6 +356,74 @@ static int64_t* invert(const int64_t* perm, int64_t N) {
     return inv;
 }
 
+/* N_pi(i) (pi-Attention, Eq. 9): the key pi positions back along the 1-D
+   pattern axis, and pi positions ahead when both directions are fetched; only
+   positions inside the sequence exist. */
+int64_t orc_partners(const orc_spec* s, const int64_t* perm, const int64_t* pos_of_token,
+                     int64_t i, int64_t* out) {
+    if (s->skip <= 0) return 0;
+    const int64_t N = orc_num_tokens(s);
+    const int hil = s->order == ORC_ORDER_HILBERT;
+    const int64_t x = hil ? pos_of_token[i] : i; /* 1-D: the token is the coordinate */
+    int64_t n = 0;
+    if (x - s->skip >= 0) out[n++] = x - s->skip;
+    if (s->skip_both && x + s->skip < N) out[n++] = x + s->skip;
+    for (int64_t a = 0; a < n; ++a)
+        if (hil) out[a] = perm[out[a]];
+    qsort(out, (size_t)n, sizeof(int64_t), cmp_i64);
+    return n;
+}
+
+/* Is token j in the ascending list set[0..n)? */
+static int contains(const int64_t* set, int64_t n, int64_t j) {
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (set[mid] < j) lo = mid + 1; else hi = mid;
+    }
+    return lo < n && set[lo] == j;
+}
+
+int64_t orc_neighbors(const orc_spec* s, const int64_t* perm, const int64_t* pos_of_token,
+                      int64_t i, int64_t* out) {
+    int64_t n = local_neighbors(s, perm, pos_of_token, i, out);
+    if (s->skip <= 0 || s->skip_mode == ORC_SKIP_SEPARATE) return n;
+    /* U(i) = N_r(i) u N_pi(i) (Eq. 8): add the partners not already local */
+    int64_t part[2];
+    const int64_t np = orc_partners(s, perm, pos_of_token, i, part);
+    const int64_t nl = n;
+    for (int64_t a = 0; a < np; ++a)
+        if (!contains(out, nl, part[a])) out[n++] = part[a];
+    if (n > nl) qsort(out, (size_t)n, sizeof(int64_t), cmp_i64);
+    return n;
+}
+
+/* The key sets over which query i takes a softmax, with an additive log-prior
+   per key (pi-Attention, Section 3.5): branch 0 is U(i) (or N_r(i) for the
+   separate variant), branch 1 exists only for the separate variant and is
+   N_pi(i).  Returns the number of keys, or -1 if the branch does not exist.
+   lp may be NULL when the caller needs no priors. */
+static int64_t branch_keys(const orc_spec* s, const int64_t* perm, const int64_t* pos, int64_t i,
+                           int branch, int64_t* nb, double* lp) {
+    const int separate = s->skip > 0 && s->skip_mode == ORC_SKIP_SEPARATE;
+    if (branch == 1 && !separate) return -1;
+    const int64_t n = branch == 0 ? orc_neighbors(s, perm, pos, i, nb)
+                                  : orc_partners(s, perm, pos, i, nb);
+    if (lp) {
+        for (int64_t a = 0; a < n; ++a) lp[a] = 0.0;
+        if (s->skip > 0 && s->skip_mode == ORC_SKIP_FIXED_FUSION && n > 0) {
+            /* delta_ij = z_ij + log(omega_ij), omega = alpha on N_r, 1 - alpha on
+               the partners (Eq. 16) */
+            int64_t* loc = (int64_t*)malloc(sizeof(int64_t) * (size_t)orc_num_tokens(s));
+            const int64_t nl = local_neighbors(s, perm, pos, i, loc);
+            for (int64_t a = 0; a < n; ++a)
+                lp[a] = contains(loc, nl, nb[a]) ? log(s->skip_prior) : log(1.0 - s->skip_prior);
+            free(loc);
+        }
+    }
+    return n;
+}
+
 int64_t orc_attended_pairs(const orc_spec* s) {
     const int64_t N = orc_num_tokens(s);
     int64_t* perm = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
@@ -362,7 +437,11 @@ int64_t orc_attended_pairs(const orc_spec* s) {
     {
         int64_t* buf = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
 #pragma omp for schedule(dynamic, 64)
-        for (int64_t i = 0; i < N; ++i) total += orc_neighbors(s, perm, pos, i, buf);
+        for (int64_t i = 0; i < N; ++i) {
+            total += orc_neighbors(s, perm, pos, i, buf);
+            if (s->skip > 0 && s->skip_mode == ORC_SKIP_SEPARATE)
+                total += orc_partners(s, perm, pos, i, buf);
+        }
         free(buf);
     }
     free(pos);
@@ -407,6 +486,7 @@ int orc_attention(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dt
         double* z = (double*)malloc(sizeof(double) * (size_t)N);
         double* qi = (double*)malloc(sizeof(double) * (size_t)D);
         double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+        double* lp = (double*)malloc(sizeof(double) * (size_t)N);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t t = 0; t < total; ++t) {
             const int64_t bh = t / nrows, r = t % nrows;
@@ -417,35 +497,40 @@ int orc_attention(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dt
             }
             const int64_t head = bh * N * D;
             for (int64_t d = 0; d < D; ++d) qi[d] = load_elem(q, dtype, head + i * D + d);
-            const int64_t n = orc_neighbors(s, perm, pos, i, nb);
             double* o = out + t * D;
-            if (n == 0) {
-                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
-                lse[t] = -INFINITY;
-                continue;
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            lse[t] = -INFINITY;
+            /* One softmax per branch (one branch unless the separate-softmax
+               variant); the output sums the branches' weighted averages. */
+            for (int branch = 0; branch < 2; ++branch) {
+                const int64_t n = branch_keys(s, perm, pos, i, branch, nb, lp);
+                if (n <= 0) continue; /* no such branch, or an empty set: adds nothing */
+                /* delta_ij = scale * q_i . k_j + log-prior  (Eq. 4, and Eq. 16 for
+                   fixed fusion) */
+                double m = -INFINITY;
+                for (int64_t a = 0; a < n; ++a) {
+                    const int64_t kj = head + nb[a] * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += qi[d] * load_elem(k, dtype, kj + d);
+                    z[a] = scale * dot + lp[a];
+                    if (z[a] > m) m = z[a];
+                }
+                /* alpha_ij = exp(delta_ij) / sum_j' exp(delta_ij') (Eq. 2, Eq. 10,
+                   Eq. 17), written with the row maximum factored out; output =
+                   sum_j alpha_ij v_j (Eq. 3, Eq. 11). */
+                double l = 0.0;
+                for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+                for (int64_t a = 0; a < n; ++a) {
+                    const double e = exp(z[a] - m);
+                    l += e;
+                    const int64_t vj = head + nb[a] * D;
+                    for (int64_t d = 0; d < D; ++d) acc[d] += e * load_elem(v, dtype, vj + d);
+                }
+                for (int64_t d = 0; d < D; ++d) o[d] += acc[d] / l;
+                if (branch == 0) lse[t] = m + log(l);
             }
-            /* z_ij = scale * q_i . k_j  (Eq. 4 with the scale passed in) */
-            double m = -INFINITY;
-            for (int64_t a = 0; a < n; ++a) {
-                const int64_t kj = head + nb[a] * D;
-                double dot = 0.0;
-                for (int64_t d = 0; d < D; ++d) dot += qi[d] * load_elem(k, dtype, kj + d);
-                z[a] = scale * dot;
-                if (z[a] > m) m = z[a];
-            }
-            /* alpha_ij = exp(z_ij) / sum_j' exp(z_ij') (Eq. 2), written with the
-               row maximum factored out; output = sum_j alpha_ij v_j (Eq. 3). */
-            double l = 0.0;
-            for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
-            for (int64_t a = 0; a < n; ++a) {
-                const double e = exp(z[a] - m);
-                l += e;
-                const int64_t vj = head + nb[a] * D;
-                for (int64_t d = 0; d < D; ++d) acc[d] += e * load_elem(v, dtype, vj + d);
-            }
-            for (int64_t d = 0; d < D; ++d) o[d] = acc[d] / l;
-            lse[t] = m + log(l);
         }
+        free(lp);
         free(acc);
         free(qi);
         free(z);
@@ -469,13 +554,16 @@ int orc_attention(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dt
      dq_i += scale dz_ij k_j,  dk_j += scale dz_ij q_i,  dv_j += P_ij dout_i.
    dqi receives dq_i (D values, added to); dk / dv (whole slices) may be NULL.
    nb, p, dp: scratch of N entries; qi, gi: scratch of D entries. */
-static void grad_row(const orc_spec* s, const int64_t* perm, const int64_t* pos, int64_t D,
-                     int32_t dtype, const void* q, const void* k, const void* v,
-                     const void* dout, double scale, int64_t head, int64_t i, double* dqi,
-                     double* dk, double* dv, int64_t* nb, double* p, double* dp, double* qi,
-                     double* gi) {
-    const int64_t n = orc_neighbors(s, perm, pos, i, nb);
-    if (n == 0) return; /* out_i = 0 does not depend on q, k, v */
+static void grad_branch(const orc_spec* s, const int64_t* perm, const int64_t* pos, int64_t D,
+                        int32_t dtype, const void* q, const void* k, const void* v,
+                        const void* dout, double scale, int64_t head, int64_t i, int branch,
+                        double* dqi, double* dk, double* dv, int64_t* nb, double* p, double* dp,
+                        double* qi, double* gi) {
+    /* the log-priors of fixed fusion are constants: they change P, not the
+       Jacobian of the softmax with respect to z.  dp holds them until the dP
+       values overwrite it. */
+    const int64_t n = branch_keys(s, perm, pos, i, branch, nb, dp);
+    if (n <= 0) return; /* out_i = 0 (or no such branch) does not depend on q, k, v */
     for (int64_t d = 0; d < D; ++d) {
         qi[d] = load_elem(q, dtype, head + i * D + d);
         gi[d] = load_elem(dout, dtype, head + i * D + d);
@@ -485,7 +573,7 @@ static void grad_row(const orc_spec* s, const int64_t* perm, const int64_t* pos,
         const int64_t kj = head + nb[a] * D;
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += qi[d] * load_elem(k, dtype, kj + d);
-        p[a] = scale * dot;
+        p[a] = scale * dot + dp[a];
         if (p[a] > m) m = p[a];
     }
     double l = 0.0;
@@ -511,6 +599,18 @@ static void grad_row(const orc_spec* s, const int64_t* perm, const int64_t* pos,
             if (dv) dv[j + d] += p[a] * gi[d];
         }
     }
+}
+
+/* All branches of query i (the separate-softmax variant has two independent
+   softmaxes whose outputs add, so their gradients add). */
+static void grad_row(const orc_spec* s, const int64_t* perm, const int64_t* pos, int64_t D,
+                     int32_t dtype, const void* q, const void* k, const void* v,
+                     const void* dout, double scale, int64_t head, int64_t i, double* dqi,
+                     double* dk, double* dv, int64_t* nb, double* p, double* dp, double* qi,
+                     double* gi) {
+    for (int branch = 0; branch < 2; ++branch)
+        grad_branch(s, perm, pos, D, dtype, q, k, v, dout, scale, head, i, branch, dqi, dk, dv, nb,
+                    p, dp, qi, gi);
 }
 
 /* Every (batch, head) slice is owned by one thread, so the scatter into dk and

@@ -64,7 +64,25 @@ typedef struct {
        to grid coordinates.  For HILBERT order a single rule (rule[0]) applied
        to the 1-D position along the curve, with axis length N. */
     orc_rule rule[3];
+    /* pi-Attention's online long-range partner ("pi-Attention", Section 3.4,
+       Eqs. 8-9; 1-D patterns only: 1-D grids or HILBERT order): query position
+       x also attends x - skip (and x + skip when skip_both), when inside the
+       sequence.  skip = 0: none.  skip_mode picks how the local set N_r and the
+       partner set N_pi are combined (Section 3.5). */
+    int64_t skip;
+    int32_t skip_both;
+    int32_t skip_mode;   /* ORC_SKIP_* */
+    double skip_prior;   /* alpha of ORC_SKIP_FIXED_FUSION, in (0, 1) */
 } orc_spec;
+
+enum {
+    ORC_SKIP_UNION = 0,        /* one softmax over U = N_r u N_pi (Eqs. 10-11) */
+    ORC_SKIP_FIXED_FUSION = 1, /* one softmax over U of z + log(alpha) on N_r keys and
+                                  z + log(1 - alpha) on the other keys (Eqs. 16-17) */
+    ORC_SKIP_SEPARATE = 2      /* a softmax over N_r and one over N_pi (Eq. 15); the output
+                                  is the sum of the two weighted averages (Eq. 11 with the
+                                  weights of Eq. 15) and lse is the N_r branch's */
+};
 
 /* Number of tokens N. */
 int64_t orc_num_tokens(const orc_spec* s);
@@ -90,13 +108,21 @@ int orc_hilbert_grid(int64_t rows, int64_t cols, int64_t* perm);
    its size. */
 int64_t orc_rule_set(const orc_rule* r, int64_t len, int64_t x, int64_t* out);
 
+/* The online partners N_pi(i) of row-major token i, ascending row-major
+   token indices; returns their number (0 without skip). */
+int64_t orc_partners(const orc_spec* s, const int64_t* perm, const int64_t* pos_of_token,
+                     int64_t i, int64_t* out);
+
 /* Neighbourhood N(i) of row-major token i, as ascending row-major token
    indices.  out must hold N entries.  pos_of_token / perm may be NULL unless
-   the order is HILBERT (they are the inverse pair from orc_order). */
+   the order is HILBERT (they are the inverse pair from orc_order).  With a
+   skip partner this is the union U(i) (Eq. 8), except for the separate-softmax
+   variant, where it is the local set N_r(i) alone. */
 int64_t orc_neighbors(const orc_spec* s, const int64_t* perm,
                       const int64_t* pos_of_token, int64_t i, int64_t* out);
 
-/* Total attended (query, key) pairs per (batch, head). */
+/* Total attended (query, key) pairs per (batch, head) (for the separate-softmax
+   variant: |N_r(i)| + |N_pi(i)| summed). */
 int64_t orc_attended_pairs(const orc_spec* s);
 
 /* Softmax attention restricted to N(i).
