@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libna.so")
 
 HOST_SOURCES = ["plan.cpp", "na_api.cpp"]
-DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "permute.hip"]
+DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "permute.hip", "pi_skip.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]

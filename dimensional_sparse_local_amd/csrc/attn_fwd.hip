@@ -44,9 +44,15 @@ namespace {
 // by more than 2^8, which keeps every P <= 256 and is exact after the final
 // division by l.
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+// Mask words of one query row for one tile: the keep plane (2 words), and with
+// BIAS the partner plane of fixed fusion (2 more words).
+template <bool BIAS> struct MaskRow { using T = u32x2; };
+template <> struct MaskRow<true> { using T = u32x4; };
+
+template <int D, int NW, bool BIAS = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(NaAttnParams p) {
+    using MaskT = typename MaskRow<BIAS>::T;
     constexpr int KV = NA_KV_BLOCK_BF16;
     constexpr int QB = 32 * NW;
     constexpr int ROW = D + 8;                   // padded LDS row (elements)
@@ -148,9 +154,18 @@ void attn_fwd_bf16(NaAttnParams p) {
         }
     };
     auto mask_row = [&](NaEntry entry) {
-        u32x2 w = {0u, 0u};
-        if (entry.mask >= 0)
-            w = gload((const u32x2*)(p.masks + ((int64_t)entry.mask * QB + mrow) * 2));
+        MaskT w = {};
+        if (entry.mask >= 0) {
+            const int64_t at = ((int64_t)entry.mask * QB + mrow) * 2;
+            const u32x2 keep = gload((const u32x2*)(p.masks + at));
+            w[0] = keep[0];
+            w[1] = keep[1];
+            if constexpr (BIAS) {
+                const u32x2 part = gload((const u32x2*)(p.skip_masks + at));
+                w[2] = part[0];
+                w[3] = part[1];
+            }
+        }
         return w;
     };
 
@@ -176,7 +191,7 @@ void attn_fwd_bf16(NaAttnParams p) {
     // 32*db + 16*(g%2) + 4*(s%4).
     const int tr_base = (half + 4 * ((lane & 15) >> 2)) * ROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    auto compute = [&](NaEntry entry, u32x2 mk, const uint16_t* kl, const uint16_t* vl) {
+    auto compute = [&](NaEntry entry, MaskT mk, const uint16_t* kl, const uint16_t* vl) {
         // S^T = K Q^T for the two 32-key halves of the tile.  All KS fragments
         // of the first half are requested up front; each MFMA of the first
         // half is then followed by the request for the matching fragment of
@@ -215,6 +230,17 @@ void attn_fwd_bf16(NaAttnParams p) {
                 const int bit = 16 * (r / 8) + 2 * ((r / 4) % 2) + 4 * (r % 4);
                 s[0][r] = keep_if(w0, bit, s[0][r]);
                 s[1][r] = keep_if(w1, bit, s[1][r]);
+            }
+            if constexpr (BIAS) {
+                // fixed fusion: partners outside the window carry the extra
+                // log-prior, as an offset of the raw dot product
+                const uint32_t b0 = mk[2] >> half, b1 = mk[3] >> half;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int bit = 16 * (r / 8) + 2 * ((r / 4) % 2) + 4 * (r % 4);
+                    s[0][r] += ((b0 >> bit) & 1u) ? p.skip_bias : 0.f;
+                    s[1][r] += ((b1 >> bit) & 1u) ? p.skip_bias : 0.f;
+                }
             }
         }
         float mx = kNegInf;
@@ -272,7 +298,7 @@ void attn_fwd_bf16(NaAttnParams p) {
     const NaEntry none = {0, -1};
     NaEntry ent_a = none, ent_b = none, ent_c = none;
     int tok_n[IPW];
-    u32x2 mk_a = {0u, 0u}, mk_b = {0u, 0u};
+    MaskT mk_a = {}, mk_b = {};
     if (e0 < e1) {
         ent_a = load_entry(p.entries + e0);
         if (e0 + 1 < e1) ent_b = load_entry(p.entries + e0 + 1);
@@ -291,7 +317,7 @@ void attn_fwd_bf16(NaAttnParams p) {
         __syncthreads();
         if (e + 1 < e1) issue(ent_b, tok_n, kn, vn);
         if (e + 2 < e1) tokens(ent_c, tok_n);
-        const u32x2 mk_c = e + 2 < e1 ? mask_row(ent_c) : u32x2{0u, 0u};
+        const MaskT mk_c = e + 2 < e1 ? mask_row(ent_c) : MaskT{};
         const NaEntry ent_d = e + 3 < e1 ? load_entry(p.entries + e + 3) : none;
         compute(ent_a, mk_a, kl, vl);
         ent_a = ent_b;
@@ -322,7 +348,8 @@ void attn_fwd_bf16(NaAttnParams p) {
             *(uint2*)(orow + d) = w;
         }
     if (p.lse && half == 0) {
-        const float lse = l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+        float lse = l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+        if constexpr (BIAS) lse += p.lse_shift;  // the log(alpha) common to every logit
         p.lse[(int64_t)bh * N + qtok] = lse;
     }
 }
@@ -738,7 +765,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(NaAttnParams p) {
 
 }  // namespace
 
-bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block) {
+bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block, bool fusion) {
+    if (fusion)  // the logit bias exists in the 32-query-per-wave bf16 kernels
+        return dtype == NA_BF16 && (head_dim == 64 || head_dim == 128) &&
+               kv_block == NA_KV_BLOCK_BF16 &&
+               (q_block == 128 || q_block == 256 || (q_block == 64 && head_dim == 64));
     if (dtype == NA_BF16)
         return (head_dim == 64 || head_dim == 128) && kv_block == NA_KV_BLOCK_BF16 &&
                (q_block == 128 || q_block == 192 || q_block == 256 ||
@@ -749,9 +780,25 @@ bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block) {
     return false;
 }
 
-int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, void* stream) {
+int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, bool fusion,
+                   void* stream) {
     hipStream_t st = (hipStream_t)stream;
     const dim3 grid((unsigned)p.n_wg);
+    if (fusion) {
+        if (head_dim == 64 && q_block == 64)
+            hipLaunchKernelGGL((attn_fwd_bf16<64, 2, true>), grid, dim3(128), 0, st, p);
+        else if (head_dim == 64 && q_block == 128)
+            hipLaunchKernelGGL((attn_fwd_bf16<64, 4, true>), grid, dim3(256), 0, st, p);
+        else if (head_dim == 64 && q_block == 256)
+            hipLaunchKernelGGL((attn_fwd_bf16<64, 8, true>), grid, dim3(512), 0, st, p);
+        else if (head_dim == 128 && q_block == 128)
+            hipLaunchKernelGGL((attn_fwd_bf16<128, 4, true>), grid, dim3(256), 0, st, p);
+        else if (head_dim == 128 && q_block == 256)
+            hipLaunchKernelGGL((attn_fwd_bf16<128, 8, true>), grid, dim3(512), 0, st, p);
+        else
+            return (int)hipErrorInvalidValue;
+        return (int)hipGetLastError();
+    }
     if (dtype == NA_BF16) {
         if (head_dim == 64 && q_block == 64)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 2>), grid, dim3(128), 0, st, p);

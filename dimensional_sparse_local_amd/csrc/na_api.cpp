@@ -3,6 +3,7 @@
 // argument checks run on the host before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -45,6 +46,7 @@ void free_device(na_plan_s* p) {
     (void)hipFree(p->d_t_row_ptr);
     (void)hipFree(p->d_t_entries);
     (void)hipFree(p->d_masks);
+    (void)hipFree(p->d_skip_masks);
     (void)hipFree(p->d_zero);
     if (cur != p->device && cur >= 0) (void)hipSetDevice(cur);
     p->d_perm = nullptr;
@@ -53,6 +55,7 @@ void free_device(na_plan_s* p) {
     p->d_t_row_ptr = nullptr;
     p->d_t_entries = nullptr;
     p->d_masks = nullptr;
+    p->d_skip_masks = nullptr;
     p->d_zero = nullptr;
     p->on_device = false;
 }
@@ -158,6 +161,7 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
         if (st == NA_OK) st = upload(p->t_row_ptr, &p->d_t_row_ptr);
         if (st == NA_OK) st = upload(p->t_entries, &p->d_t_entries);
         if (st == NA_OK) st = upload(p->masks, &p->d_masks);
+        if (st == NA_OK) st = upload(p->skip_masks, &p->d_skip_masks);
         if (st == NA_OK) {
             const std::vector<uint8_t> zeros(1024, 0);
             st = upload(zeros, (uint8_t**)&p->d_zero);
@@ -265,9 +269,15 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         return NA_ERR_INVALID_ARG;
     }
     const na_plan_desc& d = p->desc;
-    if (!na_attn_supported(d.dtype, d.head_dim, d.q_block, d.kv_block)) {
-        na_set_error("no kernel for dtype=%d head_dim=%d q_block=%d kv_block=%d", d.dtype,
-                     d.head_dim, d.q_block, d.kv_block);
+    const bool fusion = d.skip > 0 && d.skip_mode == NA_SKIP_FIXED_FUSION;
+    const bool separate = d.skip > 0 && d.skip_mode == NA_SKIP_SEPARATE;
+    if (!na_attn_supported(d.dtype, d.head_dim, d.q_block, d.kv_block, fusion)) {
+        na_set_error("no kernel for dtype=%d head_dim=%d q_block=%d kv_block=%d%s", d.dtype,
+                     d.head_dim, d.q_block, d.kv_block, fusion ? " with fixed fusion" : "");
+        return NA_ERR_UNSUPPORTED;
+    }
+    if (separate && !na_skip_supported(d.dtype, d.head_dim)) {
+        na_set_error("no partner-branch kernel for dtype=%d head_dim=%d", d.dtype, d.head_dim);
         return NA_ERR_UNSUPPORTED;
     }
     int cur = -1;
@@ -296,6 +306,15 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
     a.masks = p->d_masks;
     a.zero = p->d_zero;
     a.lse = lse;
+    if (fusion) {
+        // delta = z + log(alpha) on window keys, z + log(1 - alpha) on partners:
+        // the kernel adds log((1 - alpha) / alpha) to the partners' logits (as a
+        // raw dot-product offset) and log(alpha) to lse
+        const double alpha = d.skip_prior;
+        a.skip_masks = p->d_skip_masks;
+        a.skip_bias = (float)(std::log((1.0 - alpha) / alpha) / (double)scale);
+        a.lse_shift = (float)std::log(alpha);
+    }
     const int64_t N = p->n_tokens, D = d.head_dim, eb = elem_bytes(p);
 
     if (n_wg == 0) return NA_OK;
@@ -310,7 +329,7 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         a.v_sb = v->stride_b, a.v_sh = v->stride_h, a.v_sn = v->stride_n;
         a.o_sb = out->stride_b, a.o_sh = out->stride_h, a.o_sn = out->stride_n;
         a.perm = p->identity_order ? nullptr : p->d_perm;
-        rc = na_attn_launch(a, d.dtype, d.head_dim, d.q_block, stream);
+        rc = na_attn_launch(a, d.dtype, d.head_dim, d.q_block, fusion, stream);
     } else {
         // gather q, k, v into sequence order, attend on contiguous tiles, scatter back
         auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -335,7 +354,7 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
             a.q_sn = a.k_sn = a.v_sn = a.o_sn = D;
             a.perm = nullptr;
             a.lse = lse ? ls : nullptr;
-            rc = na_attn_launch(a, d.dtype, d.head_dim, d.q_block, stream);
+            rc = na_attn_launch(a, d.dtype, d.head_dim, d.q_block, fusion, stream);
         }
         if (rc == 0)
             rc = na_permute_launch(os, out->ptr, B, H, N, D * eb, csb, csh, csn,
@@ -344,6 +363,19 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         if (rc == 0 && lse)
             rc = na_permute_launch(ls, lse, B, H, N, 4, H * N * 4, N * 4, 4, H * N * 4, N * 4, 4,
                                    p->d_perm, 1, stream);
+    }
+    if (rc == 0 && separate) {
+        // the partner branch of the separate-softmax variant, added to out
+        NaSkipParams sp{};
+        sp.q = q->ptr, sp.k = k->ptr, sp.v = v->ptr, sp.out = out->ptr;
+        sp.q_sb = q->stride_b, sp.q_sh = q->stride_h, sp.q_sn = q->stride_n;
+        sp.k_sb = k->stride_b, sp.k_sh = k->stride_h, sp.k_sn = k->stride_n;
+        sp.v_sb = v->stride_b, sp.v_sh = v->stride_h, sp.v_sn = v->stride_n;
+        sp.o_sb = out->stride_b, sp.o_sh = out->stride_h, sp.o_sn = out->stride_n;
+        sp.batch = (int32_t)B, sp.heads = (int32_t)H, sp.n_tokens = (int32_t)N;
+        sp.skip = d.skip, sp.skip_both = d.skip_both, sp.scale = scale;
+        sp.perm = p->identity_order ? nullptr : p->d_perm;
+        rc = na_skip_launch(sp, d.dtype, d.head_dim, stream);
     }
     if (rc != 0) {
         na_set_error("kernel launch failed: %s", hip_err((hipError_t)rc));
@@ -393,6 +425,11 @@ na_status na_backward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, con
         return NA_ERR_INVALID_ARG;
     }
     const na_plan_desc& d = p->desc;
+    if (d.skip > 0 && d.skip_mode != NA_SKIP_UNION) {
+        na_set_error("gradients of the fixed-fusion and separate-softmax variants are not built "
+                     "(the union form is)");
+        return NA_ERR_UNSUPPORTED;
+    }
     if (!na_bwd_supported(d.dtype, d.head_dim, d.q_block, d.kv_block)) {
         na_set_error("no gradient kernels for dtype=%d head_dim=%d q_block=%d kv_block=%d",
                      d.dtype, d.head_dim, d.q_block, d.kv_block);

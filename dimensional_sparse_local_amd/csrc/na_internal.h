@@ -41,6 +41,12 @@ struct na_plan_s {
     int32_t mask_words = 0;         // ceil(kv_block / 32)
     std::vector<uint32_t> masks;    // [n_masks][q_block][mask_words]
     int64_t n_masks = 0;
+    // pi-Attention partner: partner_union = the partners are part of the tile
+    // map (union and fixed-fusion modes); with fixed fusion, skip_masks (same
+    // layout and ids as masks) marks the partners outside the window, whose
+    // logits carry the extra log((1 - alpha) / alpha).
+    bool partner_union = false;
+    std::vector<uint32_t> skip_masks;
     // The same tile map by key/value tile (for the gradients of K and V): for
     // key/value tile kt, entries t_row_ptr[kt] .. t_row_ptr[kt+1] of t_entries
     // hold the query tiles that attend it (field kt = query tile) in ascending
@@ -56,6 +62,7 @@ struct na_plan_s {
     int32_t* d_row_ptr = nullptr;
     NaEntry* d_entries = nullptr;
     uint32_t* d_masks = nullptr;
+    uint32_t* d_skip_masks = nullptr;
     int32_t* d_t_row_ptr = nullptr;
     NaEntry* d_t_entries = nullptr;
     void* d_zero = nullptr;   // 1 KiB of zeros
@@ -88,6 +95,12 @@ struct NaAttnParams {
     const NaEntry* entries;
     const uint32_t* masks;  // [n_masks][q_block][mask_words]
     const void* zero;       // >= 1 KiB of zeros: the source of rows past the last token
+    // fixed fusion only (else null / 0): partner bit planes, the bias added to
+    // the raw dot product q.k of a partner (log((1 - alpha) / alpha) / scale)
+    // and the shift added to lse (log alpha)
+    const uint32_t* skip_masks;
+    float skip_bias;
+    float lse_shift;
 };
 
 // Gradient launch parameters (attn_bwd.hip).  Tensors as in NaAttnParams;
@@ -133,10 +146,34 @@ bool na_bwd_supported(int dtype, int head_dim, int q_block, int kv_block);
 // Launch the three gradient kernels (row sums, dq, dk/dv); HIP error code.
 int na_bwd_launch(const NaBwdParams& p, int head_dim, void* stream);
 
-// Returns false if no variant exists for (dtype, head_dim, q_block, kv_block).
-bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block);
+// Returns false if no variant exists for (dtype, head_dim, q_block, kv_block);
+// fusion = the fixed-fusion (logit bias) variant.
+bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block, bool fusion);
 // Launch the fused attention kernel; returns the HIP error code (0 = success).
-int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, void* stream);
+int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, bool fusion,
+                   void* stream);
+
+// The partner branch of the separate-softmax variant (pi_skip.hip): for every
+// query, out += softmax over its partners of z, applied to their v rows.
+struct NaSkipParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    int64_t q_sb, q_sh, q_sn;
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t o_sb, o_sh, o_sn;
+    int32_t batch;
+    int32_t heads;
+    int32_t n_tokens;
+    int32_t skip;
+    int32_t skip_both;
+    float scale;
+    const int32_t* perm;   // null = identity addressing
+};
+bool na_skip_supported(int dtype, int head_dim);
+int na_skip_launch(const NaSkipParams& p, int dtype, int head_dim, void* stream);
 
 // Row gather / scatter (permute.hip): rows of row_bytes bytes (a multiple of 4);
 // all strides in bytes.

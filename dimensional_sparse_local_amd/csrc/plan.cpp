@@ -268,6 +268,28 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
         p->clamp[i] = d.boundary[i] == NA_BOUND_CLAMP;
         if (d.dilation[i] > 1) p->has_dilation = true;
     }
+    // pi-Attention partner
+    if (d.skip < 0 || (d.skip_both != 0 && d.skip_both != 1) || d.skip_mode < NA_SKIP_UNION ||
+        d.skip_mode > NA_SKIP_SEPARATE) {
+        na_set_error("skip must be >= 0, skip_both 0 or 1, skip_mode an NA_SKIP_* value");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (d.skip > 0 && pdims != 1) {
+        na_set_error("the skip partner is defined on one pattern dimension (1-D grids, Hilbert order)");
+        return NA_ERR_UNSUPPORTED;
+    }
+    if (d.skip > 0 && d.skip_mode == NA_SKIP_FIXED_FUSION &&
+        !(d.skip_prior > 0.f && d.skip_prior < 1.f)) {
+        na_set_error("skip_prior must lie in (0, 1) for fixed fusion");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (d.skip == 0) {
+        d.skip_both = 0;
+        d.skip_mode = NA_SKIP_UNION;
+        d.skip_prior = 0.f;
+    }
+    if (d.skip_mode != NA_SKIP_FIXED_FUSION) d.skip_prior = 0.f;
+    p->partner_union = d.skip > 0 && d.skip_mode != NA_SKIP_SEPARATE;
     p->desc = d;
     p->n_tokens = N;
     p->pdims = pdims;
@@ -333,6 +355,25 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
         }
         pairs += cnt;
     }
+    // One pattern dimension: the pattern coordinate of a position is the
+    // position itself (1-D grids in either order, and the curve position of the
+    // Hilbert order), so partners are positions pos -/+ skip.
+    const int64_t skip = d.skip;
+    auto is_partner = [&](int64_t qp, int64_t kp) {
+        return skip > 0 && (kp == qp - skip || (d.skip_both && kp == qp + skip));
+    };
+    const int32_t dil1[3] = {(int32_t)ax[0].dil, 1, 1};
+    if (skip > 0) {
+        for (int64_t pos = 0; pos < N; ++pos) {
+            for (int t = 0; t < 1 + d.skip_both; ++t) {
+                const int64_t y = t == 0 ? pos - skip : pos + skip;
+                if (y < 0 || y >= N) continue;
+                // a partner inside the window adds nothing to the union
+                if (!p->partner_union || !inside(&p->qbox[pos * 8], &p->kcoord[y * 4], 1, dil1))
+                    ++pairs;
+            }
+        }
+    }
 
     // ---- tile classification ---------------------------------------------
     const int64_t qb = d.q_block, kb = d.kv_block;
@@ -386,8 +427,15 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
             bool disjoint = false;
             for (int i = 0; i < p->pdims; ++i)
                 disjoint |= kbx[3 + i] <= ulo[i] || kbx[i] >= uhi[i];
-            if (disjoint) continue;  // empty (also when every query is empty)
-            bool full = !any_empty_query && !p->has_dilation;
+            // partners of this query tile: positions [q0, q1) shifted by -/+ skip
+            bool partners_here = false;
+            if (p->partner_union) {
+                const int64_t k0 = kt * kb, k1 = std::min(N, k0 + kb);
+                partners_here = q0 - skip < k1 && q1 - skip > k0;
+                if (d.skip_both) partners_here |= q0 + skip < k1 && q1 + skip > k0;
+            }
+            if (disjoint && !partners_here) continue;  // empty (also when every query is empty)
+            bool full = !disjoint && !any_empty_query && !p->has_dilation;
             for (int i = 0; full && i < p->pdims; ++i)
                 full = ilo[i] <= kbx[i] && kbx[3 + i] <= ihi[i];
             int cls = 2;
@@ -397,7 +445,8 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
                 const int64_t k0 = kt * kb, k1 = std::min(N, k0 + kb);
                 for (int64_t qp = q0; qp < q1 && !(hit && miss); ++qp)
                     for (int64_t kp = k0; kp < k1; ++kp) {
-                        if (inside(&p->qbox[qp * 8], &p->kcoord[kp * 4], p->pdims, dil))
+                        if (inside(&p->qbox[qp * 8], &p->kcoord[kp * 4], p->pdims, dil) ||
+                            (p->partner_union && is_partner(qp, kp)))
                             hit = true;
                         else
                             miss = true;
@@ -423,31 +472,46 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
     const int kvw = (int)ceil_div(kb, 32);
     p->mask_words = kvw;
     p->masks.clear();
+    // With fixed fusion a second plane (same id) marks the partners outside
+    // the window; a tile holding any of them always carries a mask.
+    const bool fusion = p->partner_union && d.skip_mode == NA_SKIP_FIXED_FUSION;
+    p->skip_masks.clear();
     std::unordered_map<std::string, int32_t> seen;
-    std::vector<uint32_t> m((size_t)(qb * kvw));
+    std::vector<uint32_t> m((size_t)(qb * kvw)), sk((size_t)(qb * kvw));
     for (int64_t qt = 0; qt < nqt; ++qt) {
         for (int32_t e = p->row_ptr[qt]; e < p->row_ptr[qt + 1]; ++e) {
             const int64_t kt = p->entries[e].kt;
             const bool full = p->entry_cls[e] == 2;
-            if (full && (kt + 1) * kb <= N) continue;  // no mask needed
+            const bool last = (kt + 1) * kb > N;
+            if (full && !last && !fusion) continue;  // no mask needed
             std::fill(m.begin(), m.end(), 0u);
+            std::fill(sk.begin(), sk.end(), 0u);
+            bool any_skip = false;
             for (int64_t r = 0; r < qb; ++r) {
                 const int64_t qp = qt * qb + r;
                 if (qp >= N) break;
                 for (int64_t k = 0; k < kb; ++k) {
                     const int64_t kp = kt * kb + k;
                     if (kp >= N) break;
-                    if (full || inside(&p->qbox[qp * 8], &p->kcoord[kp * 4], p->pdims, dil))
-                        m[r * kvw + k / 32] |= 1u << (k % 32);
+                    const bool in = inside(&p->qbox[qp * 8], &p->kcoord[kp * 4], p->pdims, dil);
+                    const bool part = p->partner_union && is_partner(qp, kp);
+                    if (full || in || part) m[r * kvw + k / 32] |= 1u << (k % 32);
+                    if (fusion && part && !in) {
+                        sk[r * kvw + k / 32] |= 1u << (k % 32);
+                        any_skip = true;
+                    }
                 }
             }
+            if (full && !last && !any_skip) continue;
             std::string key((const char*)m.data(), m.size() * sizeof(uint32_t));
+            if (fusion) key.append((const char*)sk.data(), sk.size() * sizeof(uint32_t));
             auto it = seen.find(key);
             int32_t id;
             if (it == seen.end()) {
                 id = (int32_t)seen.size();
                 seen.emplace(std::move(key), id);
                 p->masks.insert(p->masks.end(), m.begin(), m.end());
+                if (fusion) p->skip_masks.insert(p->skip_masks.end(), sk.begin(), sk.end());
             } else {
                 id = it->second;
             }

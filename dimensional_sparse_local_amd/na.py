@@ -23,6 +23,9 @@ NA_PLAN_HOST_ONLY = 1
 NA_FWD_PERMUTE_PASSES = 1
 
 ORDERS = {"row_major": NA_ORDER_ROW_MAJOR, "tiled": NA_ORDER_TILED, "hilbert": NA_ORDER_HILBERT}
+NA_SKIP_UNION, NA_SKIP_FIXED_FUSION, NA_SKIP_SEPARATE = 0, 1, 2
+SKIP_MODES = {"union": NA_SKIP_UNION, "fixed_fusion": NA_SKIP_FIXED_FUSION,
+              "separate": NA_SKIP_SEPARATE}
 DTYPES = {"bf16": NA_BF16, "fp32": NA_F32}
 
 I3 = ctypes.c_int32 * 3
@@ -34,6 +37,8 @@ class Desc(ctypes.Structure):
         ("window", I3), ("window_left", I3), ("stride", I3), ("dilation", I3), ("causal", I3),
         ("boundary", I3), ("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("shift", I3),
+        ("skip", ctypes.c_int32), ("skip_both", ctypes.c_int32), ("skip_mode", ctypes.c_int32),
+        ("skip_prior", ctypes.c_float),
     ]
 
 
@@ -59,7 +64,7 @@ _STATUS = {NA_ERR_INVALID_ARG: "invalid argument", NA_ERR_UNSUPPORTED: "unsuppor
            NA_ERR_PLAN_MISMATCH: "plan mismatch"}
 
 _lib = None
-ABI_VERSION = 2  # NA_ABI_VERSION of include/na.h that Desc mirrors
+ABI_VERSION = 3  # NA_ABI_VERSION of include/na.h that Desc mirrors
 
 
 def lib():
@@ -157,6 +162,11 @@ def desc_from_workload(w: dict, q_block: int = 0, kv_block: int = 0) -> Desc:
             d.boundary[i] = NA_BOUND_CLAMP
         else:
             raise ValueError("unknown pattern kind %r" % kind)
+    # pi-Attention's online partner (1-D patterns)
+    d.skip = int(pat.get("skip", 0))
+    d.skip_both = int(pat.get("skip_both", 0))
+    d.skip_mode = SKIP_MODES[pat.get("skip_mode", "union")]
+    d.skip_prior = float(pat.get("skip_prior", 0.5))
     d.q_block, d.kv_block = int(q_block), int(kv_block)
     d.head_dim = int(w["D"])
     d.dtype = DTYPES[w.get("dtype", "bf16")]

@@ -18,6 +18,9 @@ Pattern vocabulary (per grid dimension unless noted):
               (bidirectional band; causal when right = 0).
 * ``blocked`` non-overlapping windows of ``window[d]`` positions; optional
               ``shift[d]`` moves the window boundaries back (shifted windows).
+* any 1-D pattern may add pi-Attention's online partner: ``skip`` (pi),
+              ``skip_both`` (also x + pi), ``skip_mode`` ("union",
+              "fixed_fusion", "separate") and ``skip_prior`` (alpha).
 * ``sta``     sliding tile attention: tiles of ``tile[d]`` positions; the query's
               tile attends ``window_tiles[d]`` whole tiles shifted inside.
 
@@ -114,8 +117,29 @@ GNA = {
              "2 chunks of 6 frames x 3x5 tiles"),
 }
 
+# pi-Attention ("pi-Attention: Online Efficient Sparse Transformers for
+# Long-Context Modeling"): causal local window of k = 4 (Eq. 5: keys i-4 .. i)
+# plus the online partner i - pi with pi = 16 (Eqs. 8-9), the page's defaults,
+# at the Medium model's attention shape (16 heads of 64) over 8192 tokens.
+_PI = dict(B=4, H=16, D=64, dtype="bf16", grid=[8192], order="row_major")
+PI_ATTENTION = {
+    "pi_union_bf16": dict(
+        _PI, name="pi_union_bf16", seed=31,
+        pattern=dict(kind="band", left=4, right=0, skip=16, skip_mode="union"),
+        note="pi-Attention, one softmax over window u partner (Eq. 11), k=4, pi=16, 8192 tokens"),
+    "pi_fusion_bf16": dict(
+        _PI, name="pi_fusion_bf16", seed=32,
+        pattern=dict(kind="band", left=4, right=0, skip=16, skip_mode="fixed_fusion",
+                     skip_prior=0.5),
+        note="pi-Attention fixed fusion (Eqs. 16-17), alpha=0.5, k=4, pi=16, 8192 tokens"),
+    "pi_separate_bf16": dict(
+        _PI, name="pi_separate_bf16", seed=33,
+        pattern=dict(kind="band", left=4, right=0, skip=16, skip_mode="separate"),
+        note="pi-Attention separate softmax (Eq. 15), k=4, pi=16, 8192 tokens"),
+}
+
 # Every named workload.
-ALL = {**CONFIGS, **HILBERT_PAGE, **GNA}
+ALL = {**CONFIGS, **HILBERT_PAGE, **GNA, **PI_ATTENTION}
 
 # The workload the benchmark times by default (the headline metric's config).
 HEADLINE = "sta3d_bf16"

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define NA_ABI_VERSION 2
+#define NA_ABI_VERSION 3
 
 typedef enum {
     NA_OK = 0,
@@ -73,6 +73,19 @@ enum {
                                travel direction) at even cut points where possible, so every step
                                is to a 4-neighbour unless cols is odd and rows even (then exactly
                                one step is diagonal) */
+};
+
+/* How pi-Attention's online partner combines with the local window
+ * ("pi-Attention: Online Efficient Sparse Transformers for Long-Context
+ * Modeling", Sections 3.4-3.5). */
+enum {
+    NA_SKIP_UNION = 0,        /* one softmax over the union of the window and the partners
+                                 (Eqs. 8-11) */
+    NA_SKIP_FIXED_FUSION = 1, /* one softmax over the union of z + log(alpha) on window keys and
+                                 z + log(1 - alpha) on partners outside the window (Eqs. 16-17);
+                                 lse is the log-sum-exp of those logits */
+    NA_SKIP_SEPARATE = 2      /* a softmax over the window and one over the partners (Eq. 15);
+                                 out is the sum of the two weighted averages, lse the window's */
 };
 
 /* Border rule of a pattern dimension. */
@@ -130,6 +143,13 @@ typedef struct {
                                [k*stride - shift, (k+1)*stride - shift).  With stride = window and
                                truncation, shift = window / 2 gives shifted (Swin-style) windows,
                                the shifted-window form of the Hilbert page's window attention */
+    int32_t skip;           /* pi-Attention's online long-range partner (Eqs. 8-9): a query at
+                               pattern position x also attends x - skip (0 = no partner); only for
+                               one pattern dimension (1-D grids, Hilbert order), else
+                               NA_ERR_UNSUPPORTED; partners outside the sequence do not exist */
+    int32_t skip_both;      /* 1: also x + skip (bidirectional) */
+    int32_t skip_mode;      /* NA_SKIP_* */
+    float skip_prior;       /* alpha of NA_SKIP_FIXED_FUSION, 0 < alpha < 1 */
 } na_plan_desc;
 
 typedef struct {
@@ -137,7 +157,9 @@ typedef struct {
     int64_t q_block, kv_block;
     int64_t n_q_tiles, n_kv_tiles;
     int64_t n_empty, n_partial, n_full; /* over all n_q_tiles * n_kv_tiles pairs */
-    int64_t attended_pairs;             /* sum over queries of |neighbourhood|, per (batch, head) */
+    int64_t attended_pairs;             /* sum over queries of |neighbourhood|, per (batch, head);
+                                           with a skip partner |window u partners|, or
+                                           |window| + |partners| for NA_SKIP_SEPARATE */
 } na_plan_stats;
 
 typedef struct {
@@ -181,7 +203,9 @@ size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t
  * NA_ERR_UNSUPPORTED if no kernel matches (dtype, head_dim, q_block,
  * kv_block): bf16 with head_dim 64 or 128 and (q_block, kv_block) =
  * (128, 64), (192, 64) or (256, 64), and (64, 64) at head_dim 64; fp32 with head_dim 32 or
- * 64 and (32, 32).
+ * 64 and (32, 32).  Fixed fusion (NA_SKIP_FIXED_FUSION) runs in bf16 only, at q_block 128
+ * or 256 (or 64 at head_dim 64).  The separate-softmax mode enqueues a second kernel
+ * after the attention kernel: it adds each query's partner softmax to out.
  * In bf16 the probabilities are rounded to bf16 before they enter both P.V and
  * the row sum, so lse carries a relative row-sum error of at most 2^-8. */
 na_status na_forward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
@@ -208,8 +232,10 @@ size_t na_backward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H);
  * must not overlap the inputs.  workspace: >= na_backward_workspace_bytes,
  * 256-byte aligned, caller-owned; no allocation happens.  bf16 only, head_dim
  * 64 or 128, (q_block, kv_block) = (128, 64) or (256, 64); other plans return
- * NA_ERR_UNSUPPORTED.  P and dS are rounded to bf16 before their MFMA
- * products, accumulation is fp32.  Asynchronous on stream. */
+ * NA_ERR_UNSUPPORTED, and so do plans with a skip partner in the fixed-fusion
+ * or separate-softmax mode (the union mode is an ordinary neighbourhood).  P
+ * and dS are rounded to bf16 before their MFMA products, accumulation is fp32.
+ * Asynchronous on stream. */
 na_status na_backward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
                       const na_tensor* k, const na_tensor* v, const na_tensor* out,
                       const na_tensor* dout, const float* lse, const na_tensor* dq,

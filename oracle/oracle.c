@@ -740,6 +740,10 @@ int orc_tile_classes(const orc_spec* s, int64_t q_block, int64_t kv_block, uint8
                 const int64_t n = orc_neighbors(s, perm, pos, perm[p], nb);
                 total += n;
                 for (int64_t a = 0; a < n; ++a) row[pos[nb[a]] / kv_block] += 1;
+                /* the separate variant's partners are attended outside the tile
+                   map, but count as attended pairs */
+                if (s->skip > 0 && s->skip_mode == ORC_SKIP_SEPARATE)
+                    total += orc_partners(s, perm, pos, perm[p], nb);
             }
         }
         free(nb);

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = na.lib()
-    assert lib.na_abi_version() == na.ABI_VERSION == 2
+    assert lib.na_abi_version() == na.ABI_VERSION == 3
     for s in range(6):
         assert lib.na_status_string(s)
     assert lib.na_status_string(99) == b"unknown status"

@@ -267,3 +267,58 @@ def test_speedup_bounds():
     sb = na.Plan(dict(grid=[100], pattern=dict(kind="band", left=100, right=100), D=64,
                       dtype="bf16"), host_only=True, q_block=128).speedup_bounds()
     assert sb == {"flop": 1.0, "tile": 1.0, "useful_fraction": 1.0}
+
+
+def test_pi_partner_tile_maps():
+    """pi-Attention's partner (pi-Attention, Eqs. 8-9) in the tile map: union
+    and fixed fusion put the partners into the map, the separate variant keeps
+    the window's map and counts the partners as attended pairs."""
+    rng = np.random.default_rng(77)
+    for it in range(120):
+        mode = ["union", "fixed_fusion", "separate"][it % 3]
+        skip = int(rng.integers(1, 80))
+        both = int(rng.integers(0, 2))
+        if rng.random() < 0.3:
+            side = int(rng.integers(2, 12))
+            wl = dict(grid=[side, int(rng.integers(2, 12))], order="hilbert")
+        else:
+            wl = dict(grid=[int(rng.integers(1, 300))])
+        base = rng.choice(["band", "na", "blocked"])
+        if base == "band":
+            pat = dict(kind="band", left=int(rng.integers(0, 20)), right=int(rng.integers(0, 5)))
+        elif base == "na":
+            pat = dict(kind="na", window=[int(rng.integers(1, 30))])
+        else:
+            pat = dict(kind="blocked", window=[int(rng.integers(1, 30))])
+        pat.update(skip=skip, skip_both=both, skip_mode=mode, skip_prior=0.3)
+        wl["pattern"] = pat
+        n = oracle.num_tokens(wl)
+        qb = int(rng.choice([16, 32, 64, 128]))
+        kb = int(rng.choice([16, 32, 64]))
+        try:
+            _compare(wl, qb, kb)
+        except AssertionError as e:
+            raise AssertionError("workload %r qb=%d kb=%d: %s" % (wl, qb, kb, e))
+
+
+@pytest.mark.parametrize("pattern,status", [
+    (dict(kind="na", window=[3, 3], skip=4), "unsupported"),          # two pattern dimensions
+    (dict(kind="na", window=[3, 3], skip=-1), "invalid"),
+    (dict(kind="na", window=[3, 3], skip=4, skip_both=2), "invalid"),
+])
+def test_pi_partner_invalid_2d(pattern, status):
+    d = na.desc_from_workload(dict(grid=[6, 6], pattern=pattern, D=64, dtype="bf16"))
+    with pytest.raises(na.NaError) as ei:
+        na.Plan(d, host_only=True)
+    want = na.NA_ERR_UNSUPPORTED if status == "unsupported" else na.NA_ERR_INVALID_ARG
+    assert ei.value.status == want
+
+
+@pytest.mark.parametrize("prior", [0.0, 1.0, -0.5, float("nan")])
+def test_pi_fixed_fusion_needs_prior_in_open_interval(prior):
+    d = na.desc_from_workload(dict(grid=[64], D=64, dtype="bf16",
+                                   pattern=dict(kind="band", left=4, right=0, skip=16,
+                                                skip_mode="fixed_fusion", skip_prior=prior)))
+    with pytest.raises(na.NaError) as ei:
+        na.Plan(d, host_only=True)
+    assert ei.value.status == na.NA_ERR_INVALID_ARG
