@@ -32,15 +32,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def read_traffic(kernel_sig: str, workload: str):
+def read_traffic(kernel_sig: str, workload: str, q_block: int):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
-    was taken on the current kernel source and this workload (null otherwise)."""
+    was taken on the current kernel source, this workload and query tile (null
+    otherwise)."""
     try:
         with open(PROFILE_PMC) as f:
             for line in f:
                 if line.startswith("traffic_json:"):
                     d = json.loads(line.split(":", 1)[1])
-                    if d.get("kernel_sig") == kernel_sig and d.get("workload") == workload:
+                    if (d.get("kernel_sig") == kernel_sig and d.get("workload") == workload
+                            and d.get("q_block", 256) == q_block):
                         return d.get("bytes_per_launch")
     except OSError:
         pass
@@ -95,7 +97,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
-    ap.add_argument("--q-block", type=int, default=0)
+    ap.add_argument("--q-block", type=int, default=0,
+                    help="query tile; 0 = the forward pass takes 384 at head_dim 128 when every "
+                         "visited tile pair is full at 384 (sliding-tile maps: each staged K/V "
+                         "tile then serves 1.5x the queries), else the library default")
     ap.add_argument("--permute-passes", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,7 +146,11 @@ def main():
     B, H, D = int(wl["B"]), int(wl["H"]), int(wl["D"])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    plan = na.Plan(wl, q_block=args.q_block)
+    q_block = args.q_block
+    if q_block == 0 and args.which == "forward" and D == 128 and wl["dtype"] == "bf16":
+        if na.Plan(wl, host_only=True, q_block=384).stats["n_partial"] == 0:
+            q_block = 384
+    plan = na.Plan(wl, q_block=q_block)
     flops = plan.effective_flops(B, H)
     q, k, v = W.make_qkv(wl, device=dev)
     scale = W.default_scale(wl)
@@ -200,7 +209,7 @@ def main():
             dense_pat = dict(kind="band", left=n_tok, right=n_tok)
         else:
             dense_pat = dict(kind="na", window=list(wl["grid"]))
-        dense = na.Plan(W.scaled(wl, pattern=dense_pat), q_block=args.q_block)
+        dense = na.Plan(W.scaled(wl, pattern=dense_pat), q_block=q_block)
         dense_out = torch.empty_like(q)
         dense_lse = torch.empty_like(lse)
 
@@ -234,7 +243,7 @@ def main():
     else:
         metric = "effective TFLOP/s (unmasked FLOPs), %s%s" % (
             wl.get("note", name), ", backward pass" if args.which == "backward" else "")
-    traffic = read_traffic(sig, name) if args.which == "forward" else None
+    traffic = read_traffic(sig, name, plan.stats["q_block"]) if args.which == "forward" else None
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}

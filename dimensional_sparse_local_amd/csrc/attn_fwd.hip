@@ -23,7 +23,11 @@ namespace {
 // bf16: NW waves of 32 queries each (query tile 32*NW), key/value tile 64.
 //
 // Two waves share every SIMD (<= 256 registers each), so the MFMA phase of one
-// overlaps the softmax phase of the other.  K and V tiles travel from HBM/L2
+// overlaps the softmax phase of the other.  With 12 waves (384 queries: one
+// 6x8x8 sliding tile) three waves share a SIMD (<= 168 registers): each K/V
+// tile staged from L2 then serves 1.5 times the queries, which is what limits
+// these kernels (staging the tiles, not the barriers or the waits, costs about
+// a third of the time at 256 queries).  K and V tiles travel from HBM/L2
 // straight into LDS (global_load_lds, 16 bytes per lane, no register staging)
 // into two statically selected buffers: while tile e is computed from one
 // buffer, tile e+1 streams into the other.  The gather addresses are prepared
@@ -50,7 +54,8 @@ template <bool BIAS> struct MaskRow { using T = u32x2; };
 template <> struct MaskRow<true> { using T = u32x4; };
 
 template <int D, int NW, bool BIAS = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : 2, NW > 8 ? 3 : 2)))
 void attn_fwd_bf16(NaAttnParams p) {
     using MaskT = typename MaskRow<BIAS>::T;
     constexpr int KV = NA_KV_BLOCK_BF16;
@@ -199,7 +204,19 @@ void attn_fwd_bf16(NaAttnParams p) {
         f32x16 s[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.f;
-        {
+        if constexpr (NW > 8) {
+            // three waves per SIMD (168 registers): one K fragment in flight,
+            // the compiler schedules the reads ahead as registers allow
+            const uint16_t* kr0 = kl + kappa * ROW + 8 * half;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 kf = *(const bf16x8*)(kr0 + 32 * ROW * kb + 16 * ks);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+                }
+            }
+        } else {
             const uint16_t* kr0 = kl + kappa * ROW + 8 * half;
             const uint16_t* kr1 = kr0 + 32 * ROW;
             bf16x8 kf[KS];
@@ -773,7 +790,7 @@ bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block, bool 
     if (dtype == NA_BF16)
         return (head_dim == 64 || head_dim == 128) && kv_block == NA_KV_BLOCK_BF16 &&
                (q_block == 128 || q_block == 192 || q_block == 256 ||
-                (q_block == 64 && head_dim == 64));
+                (q_block == 64 && head_dim == 64) || (q_block == 384 && head_dim == 128));
     if (dtype == NA_F32)
         return (head_dim == 32 || head_dim == 64) && kv_block == NA_KV_BLOCK_F32 &&
                q_block == NA_Q_BLOCK_F32;
@@ -806,6 +823,8 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
             hipLaunchKernelGGL((attn_fwd_bf16<128, 4>), grid, dim3(256), 0, st, p);
         else if (head_dim == 128 && q_block == 256)
             hipLaunchKernelGGL((attn_fwd_bf16<128, 8>), grid, dim3(512), 0, st, p);
+        else if (head_dim == 128 && q_block == 384)
+            hipLaunchKernelGGL((attn_fwd_bf16<128, 12>), grid, dim3(768), 0, st, p);
         else if (head_dim == 64 && q_block == 128)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 4>), grid, dim3(256), 0, st, p);
         else if (head_dim == 64 && q_block == 256)

@@ -161,6 +161,23 @@ def test_d128_q256(wl):
     _run(wl, q_block=256)
 
 
+@pytest.mark.parametrize("wl", D128_QB256, ids=[w["name"] for w in D128_QB256])
+def test_d128_q384(wl):
+    """Twelve waves of 32 queries (three per SIMD) on the same cases."""
+    _run(wl, q_block=384)
+
+
+@pytest.mark.parametrize("name", ["sta3d_bf16", "sta3d_causal_t_bf16"])
+def test_full_size_q384(name):
+    """The sliding-tile workloads as the benchmark launches their forward pass:
+    384-query tiles, every visited tile pair full."""
+    wl = W.ALL[name]
+    from dimensional_sparse_local_amd import na
+
+    assert na.Plan(wl, host_only=True, q_block=384).stats["n_partial"] == 0
+    _run(wl, rows=_sample_rows(wl, 24, seed=wl["seed"] + 1), q_block=384)
+
+
 def test_hilbert_permute_passes():
     wl = W.scaled(W.CONFIGS["hilbert_band_bf16"], name="hilbert_passes", B=1, H=3,
                   grid=[32, 32], pattern=dict(kind="band", left=40, right=40))
