@@ -293,12 +293,15 @@ void attn_bwd_dq(NaBwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: one workgroup per key/value tile (64 keys) of one (batch, head), two
-// waves of 32 keys.  The tile's keys and values stay in registers as B
-// operands; the workgroup walks the query tiles that attend the tile (the
-// plan's transposed map) in steps of 32 queries, staging their q and dout rows
-// in LDS by DMA (double-buffered, the next step in flight) together with their
-// lse, delta and mask words.  Per step, with the roles of the forward swapped
+// dk, dv: one workgroup per pair of key/value tiles (128 keys) of one (batch,
+// head), four waves of 32 keys (one per SIMD).  The keys and values stay in
+// registers as B operands; the workgroup walks the query tiles that attend
+// either tile (the plan's paired key-major map) in steps of 32 queries,
+// staging their q and dout rows in LDS by DMA (double-buffered, the next step
+// in flight) together with their lse, delta and the mask words of both tiles.
+// Staging one step for 128 keys instead of 64 halves the staged bytes per
+// flop, which is what bounds this kernel.  A wave whose tile the step's query
+// tile does not attend skips the step's arithmetic.  Per step, with the roles of the forward swapped
 // (lane = key, q / dout rows permuted inside the MFMA block):
 //     S = Q K^T,  dP = dout V^T               (q and dout rows as A operands),
 //     P = exp2(S scale log2 e - lse log2 e),  dS = P (dP - delta),
@@ -308,10 +311,11 @@ void attn_bwd_dq(NaBwdParams p) {
 // that order so that each lane reads its sixteen as four 16-byte words.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))  // 192 / 294 registers
 void attn_bwd_dkdv(NaBwdParams p) {
     constexpr int KV = NA_KV_BLOCK_BF16;
-    constexpr int NW = 2;
+    constexpr int NW = 4;
     constexpr int QS = 32;                       // queries per step
     constexpr int ROW = D + 8;
     constexpr int CS = D / 8 + 1;
@@ -322,7 +326,7 @@ void attn_bwd_dkdv(NaBwdParams p) {
     static_assert(2 * RSLOT % 64 == 0, "q and dout rows fill whole DMA blocks");
     constexpr int BPW = (NBLK + NW - 1) / NW;
     constexpr int RE = 2 * QS * ROW;             // LDS elements of a step's rows
-    constexpr int AUX = 2 * QS + 2 * QS;         // lse (log2), delta, mask words [QS][2]
+    constexpr int AUX = 2 * QS + 4 * QS;         // lse (log2), delta, mask words [2][QS][2]
 
     __shared__ __attribute__((aligned(1024))) uint16_t rows0[RE];
     __shared__ __attribute__((aligned(1024))) uint16_t rows1[RE];
@@ -334,10 +338,11 @@ void attn_bwd_dkdv(NaBwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
 
-    const int n_wg = p.n_kv_tiles * p.batch * p.heads;
+    const int n_pairs = (p.n_kv_tiles + 1) / 2;
+    const int n_wg = n_pairs * p.batch * p.heads;
     const int wg = xcd_remap(blockIdx.x, n_wg);
-    const int kt = wg % p.n_kv_tiles;
-    const int bh = wg / p.n_kv_tiles;
+    const int kg = wg % n_pairs;              // key tiles 2 kg and 2 kg + 1
+    const int bh = wg / n_pairs;
     const int b = bh / p.heads, h = bh % p.heads;
     const int N = p.n_tokens;
     const int QBK = p.q_block;
@@ -345,7 +350,7 @@ void attn_bwd_dkdv(NaBwdParams p) {
     const float c = p.scale_log2;
 
     // ---- this lane's key ------------------------------------------------------
-    const int kpos = kt * KV + 32 * wave + l32;
+    const int kpos = kg * 2 * KV + 32 * wave + l32;   // waves 0-1: tile 2 kg, 2-3: 2 kg + 1
     const bool kvalid = kpos < N;
     const int ktok = kvalid ? (p.perm ? p.perm[kpos] : kpos) : 0;
     bf16x8 kf[KS], vf[KS];
@@ -373,17 +378,19 @@ void attn_bwd_dkdv(NaBwdParams p) {
         for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
 
     // ---- steps: (entry e of the transposed row, 32-query sub-block sb) --------
-    const int t0 = cload(p.t_row_ptr + kt), t1 = cload(p.t_row_ptr + kt + 1);
+    const int t0 = cload(p.p_row_ptr + kg), t1 = cload(p.p_row_ptr + kg + 1);
     struct Step {
-        int e, sb, qt, mask;
+        int e, sb, qt, mask0, mask1;
+    };
+    auto load_pair = [&](int e, Step& st) {
+        const i32x4 v = cload((const i32x4*)(p.p_entries + e));
+        st.qt = v[0];
+        st.mask0 = v[1];
+        st.mask1 = v[2];
     };
     auto first_step = [&]() {
-        Step st{t0, 0, 0, -1};
-        if (t0 < t1) {
-            const NaEntry en = load_entry(p.t_entries + t0);
-            st.qt = en.kt;
-            st.mask = en.mask;
-        }
+        Step st{t0, 0, 0, -1, -1};
+        if (t0 < t1) load_pair(t0, st);
         return st;
     };
     auto next_step = [&](Step st) {
@@ -392,11 +399,7 @@ void attn_bwd_dkdv(NaBwdParams p) {
         } else {
             ++st.e;
             st.sb = 0;
-            if (st.e < t1) {
-                const NaEntry en = load_entry(p.t_entries + st.e);
-                st.qt = en.kt;
-                st.mask = en.mask;
-            }
+            if (st.e < t1) load_pair(st.e, st);
         }
         return st;
     };
@@ -432,19 +435,24 @@ void attn_bwd_dkdv(NaBwdParams p) {
     // lse / delta / mask words of a step, fetched into registers by wave 0 and
     // written to LDS at the end of the previous step: lane t < 32 holds query t
     // (stored at the accumulator position of query t), lane l holds mask word
-    // (row l / 2, word l % 2), all ones for a tile without a mask.
-    auto aux_fetch = [&](Step st, float* lv, float* dl, uint32_t* mw) {
+    // (row l / 2, word l % 2) of each tile: all ones for a tile without a mask,
+    // zero for a tile the query tile does not attend.
+    auto mask_word = [&](int mask, int sb) -> uint32_t {
+        if (mask == -1) return ~0u;
+        if (mask < 0) return 0u;
+        return gload(p.masks + ((int64_t)mask * QBK + sb * QS + (lane >> 1)) * 2 + (lane & 1));
+    };
+    auto aux_fetch = [&](Step st, float* lv, float* dl, uint32_t* mw0, uint32_t* mw1) {
         const int t = lane & 31;
         const int qp = st.qt * QBK + st.sb * QS + t;
         const bool valid = qp < N;
         const int tok = valid ? (p.perm ? gload(p.perm + qp) : qp) : 0;
         *lv = lse_log2(valid ? gload(p.lse + (int64_t)bh * N + tok) : 0.f, valid);
         *dl = valid ? gload(p.delta + (int64_t)bh * N + tok) : 0.f;
-        *mw = st.mask >= 0 ? gload(p.masks + ((int64_t)st.mask * QBK + st.sb * QS + (lane >> 1)) * 2 +
-                                   (lane & 1))
-                           : ~0u;
+        *mw0 = mask_word(st.mask0, st.sb);
+        *mw1 = mask_word(st.mask1, st.sb);
     };
-    auto aux_store = [&](float lv, float dl, uint32_t mw, float* aux) {
+    auto aux_store = [&](float lv, float dl, uint32_t mw0, uint32_t mw1, float* aux) {
         const int t = lane & 31;
         const int a = t >> 4, rem = t & 15;
         const int pos = 16 * (rem & 1) + 8 * a + 4 * ((rem >> 1) & 1) + (rem >> 2);
@@ -452,13 +460,16 @@ void attn_bwd_dkdv(NaBwdParams p) {
             aux[pos] = lv;
             aux[QS + pos] = dl;
         }
-        ((uint32_t*)aux)[2 * QS + lane] = mw;
+        ((uint32_t*)aux)[2 * QS + lane] = mw0;
+        ((uint32_t*)aux)[4 * QS + lane] = mw1;
     };
 
     const int kappa = 16 * (l32 >> 4) + 2 * ((l32 >> 3) & 1) + ((l32 >> 2) & 1) + 4 * (l32 & 3);
     const int tr_base = (half + 4 * ((lane & 15) >> 2)) * ROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     auto compute = [&](Step st, const uint16_t* rl, const float* aux) {
+        const int my_mask = wave >= 2 ? st.mask1 : st.mask0;   // wave-uniform
+        if (my_mask == NA_MASK_NONE) return;   // this wave's tile is not attended by the step
         const uint16_t* ql = rl;
         const uint16_t* gl = rl + QS * ROW;
         f32x16 s, dp;
@@ -474,8 +485,8 @@ void attn_bwd_dkdv(NaBwdParams p) {
                                                              0, 0);
             }
         }
-        const uint32_t* mrows = (const uint32_t*)aux + 2 * QS;
-        const bool masked = st.mask >= 0;
+        const uint32_t* mrows = (const uint32_t*)aux + 2 * QS + (wave >= 2 ? 2 * QS : 0);
+        const bool masked = my_mask >= 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const f32x4 lv = *(const f32x4*)(aux + 16 * half + 4 * i);
@@ -486,7 +497,7 @@ void attn_bwd_dkdv(NaBwdParams p) {
                 float pr = fast_exp2(__builtin_fmaf(s[r], c, -lv[j]));
                 if (masked) {
                     const int q = 16 * (r / 8) + 2 * ((r / 4) % 2) + half + 4 * (r % 4);
-                    pr = (mrows[2 * q + wave] >> l32) & 1u ? pr : 0.f;
+                    pr = (mrows[2 * q + (wave & 1)] >> l32) & 1u ? pr : 0.f;
                 }
                 s[r] = pr;
                 dp[r] = pr * (dp[r] - dl[j]);
@@ -525,10 +536,10 @@ void attn_bwd_dkdv(NaBwdParams p) {
         tokens(cur, tok);
         issue(tok, rows0);
         float lv, dl;
-        uint32_t mw;
+        uint32_t mw0, mw1;
         if (wave == 0) {
-            aux_fetch(cur, &lv, &dl, &mw);
-            aux_store(lv, dl, mw, aux0);
+            aux_fetch(cur, &lv, &dl, &mw0, &mw1);
+            aux_store(lv, dl, mw0, mw1, aux0);
         }
         int tok_n[BPW];
         if (nx.e < t1) tokens(nx, tok_n);
@@ -538,11 +549,11 @@ void attn_bwd_dkdv(NaBwdParams p) {
             const Step nn = nx.e < t1 ? next_step(nx) : nx;
             if (nx.e < t1) {
                 issue(tok_n, rn);
-                if (wave == 0) aux_fetch(nx, &lv, &dl, &mw);
+                if (wave == 0) aux_fetch(nx, &lv, &dl, &mw0, &mw1);
                 if (nn.e < t1) tokens(nn, tok_n);
             }
             compute(cur, rl, al);
-            if (nx.e < t1 && wave == 0) aux_store(lv, dl, mw, an);
+            if (nx.e < t1 && wave == 0) aux_store(lv, dl, mw0, mw1, an);
             cur = nx;
             nx = nn;
         };
@@ -573,21 +584,21 @@ int na_bwd_launch(const NaBwdParams& p, int head_dim, void* stream) {
     const int lanes = head_dim / 8;
     const dim3 gd((unsigned)((rows * lanes + 255) / 256));
     const dim3 gq((unsigned)((int64_t)p.n_q_tiles * p.batch * p.heads));
-    const dim3 gk((unsigned)((int64_t)p.n_kv_tiles * p.batch * p.heads));
+    const dim3 gk((unsigned)((int64_t)((p.n_kv_tiles + 1) / 2) * p.batch * p.heads));
     if (head_dim == 128) {
         hipLaunchKernelGGL((bwd_delta<128>), gd, dim3(256), 0, st, p);
         if (p.q_block == 256)
             hipLaunchKernelGGL((attn_bwd_dq<128, 8>), gq, dim3(512), 0, st, p);
         else
             hipLaunchKernelGGL((attn_bwd_dq<128, 4>), gq, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((attn_bwd_dkdv<128>), gk, dim3(128), 0, st, p);
+        hipLaunchKernelGGL((attn_bwd_dkdv<128>), gk, dim3(256), 0, st, p);
     } else if (head_dim == 64) {
         hipLaunchKernelGGL((bwd_delta<64>), gd, dim3(256), 0, st, p);
         if (p.q_block == 256)
             hipLaunchKernelGGL((attn_bwd_dq<64, 8>), gq, dim3(512), 0, st, p);
         else
             hipLaunchKernelGGL((attn_bwd_dq<64, 4>), gq, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((attn_bwd_dkdv<64>), gk, dim3(128), 0, st, p);
+        hipLaunchKernelGGL((attn_bwd_dkdv<64>), gk, dim3(256), 0, st, p);
     } else {
         return (int)hipErrorInvalidValue;
     }

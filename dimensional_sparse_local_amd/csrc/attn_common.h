@@ -48,6 +48,7 @@ __device__ __forceinline__ T cload(const T* ptr) {
 }
 
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ NaEntry load_entry(const NaEntry* e) {
     const i32x2 v = cload((const i32x2*)e);
     return NaEntry{v[0], v[1]};

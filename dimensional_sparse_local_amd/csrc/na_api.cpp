@@ -45,6 +45,8 @@ void free_device(na_plan_s* p) {
     (void)hipFree(p->d_entries);
     (void)hipFree(p->d_t_row_ptr);
     (void)hipFree(p->d_t_entries);
+    (void)hipFree(p->d_p_row_ptr);
+    (void)hipFree(p->d_p_entries);
     (void)hipFree(p->d_masks);
     (void)hipFree(p->d_skip_masks);
     (void)hipFree(p->d_zero);
@@ -54,6 +56,8 @@ void free_device(na_plan_s* p) {
     p->d_entries = nullptr;
     p->d_t_row_ptr = nullptr;
     p->d_t_entries = nullptr;
+    p->d_p_row_ptr = nullptr;
+    p->d_p_entries = nullptr;
     p->d_masks = nullptr;
     p->d_skip_masks = nullptr;
     p->d_zero = nullptr;
@@ -160,6 +164,8 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
         if (st == NA_OK) st = upload(p->entries, &p->d_entries);
         if (st == NA_OK) st = upload(p->t_row_ptr, &p->d_t_row_ptr);
         if (st == NA_OK) st = upload(p->t_entries, &p->d_t_entries);
+        if (st == NA_OK) st = upload(p->p_row_ptr, &p->d_p_row_ptr);
+        if (st == NA_OK) st = upload(p->p_entries, &p->d_p_entries);
         if (st == NA_OK) st = upload(p->masks, &p->d_masks);
         if (st == NA_OK) st = upload(p->skip_masks, &p->d_skip_masks);
         if (st == NA_OK) {
@@ -471,6 +477,8 @@ na_status na_backward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, con
     a.entries = p->d_entries;
     a.t_row_ptr = p->d_t_row_ptr;
     a.t_entries = p->d_t_entries;
+    a.p_row_ptr = p->d_p_row_ptr;
+    a.p_entries = p->d_p_entries;
     a.masks = p->d_masks;
     a.zero = p->d_zero;
     if (p->n_tokens == 0) return NA_OK;

@@ -21,6 +21,17 @@ struct NaEntry {
     int32_t mask;
 };
 
+// One query tile of the paired key-major map (gradients of K and V): the
+// query tile and the mask ids for the two key/value tiles of the pair
+// (-1 = every pair attended, -2 = the query tile does not attend that tile).
+struct NaPairEntry {
+    int32_t qt;
+    int32_t mask0;
+    int32_t mask1;
+    int32_t pad;
+};
+constexpr int32_t NA_MASK_NONE = -2;
+
 struct na_plan_s {
     na_plan_desc desc;        // normalised copy (defaults filled in)
     int64_t n_tokens = 0;
@@ -53,6 +64,10 @@ struct na_plan_s {
     // order, with the mask ids of the query-major map.
     std::vector<int32_t> t_row_ptr; // n_kv_tiles + 1
     std::vector<NaEntry> t_entries;
+    // The same by pairs of key/value tiles (2g, 2g + 1): the union of their
+    // query tiles in ascending order, with both mask ids.
+    std::vector<int32_t> p_row_ptr; // ceil(n_kv_tiles / 2) + 1
+    std::vector<NaPairEntry> p_entries;
     na_plan_stats stats{};
 
     // device copies (null when host-only or not needed)
@@ -65,6 +80,8 @@ struct na_plan_s {
     uint32_t* d_skip_masks = nullptr;
     int32_t* d_t_row_ptr = nullptr;
     NaEntry* d_t_entries = nullptr;
+    int32_t* d_p_row_ptr = nullptr;
+    NaPairEntry* d_p_entries = nullptr;
     void* d_zero = nullptr;   // 1 KiB of zeros
 };
 
@@ -137,6 +154,8 @@ struct NaBwdParams {
     const NaEntry* entries;
     const int32_t* t_row_ptr;
     const NaEntry* t_entries;
+    const int32_t* p_row_ptr;     // paired key-major map
+    const NaPairEntry* p_entries;
     const uint32_t* masks;
     const void* zero;      // >= 1 KiB of zeros
 };

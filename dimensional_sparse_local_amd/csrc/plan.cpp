@@ -531,6 +531,27 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
             for (int32_t e = p->row_ptr[qt]; e < p->row_ptr[qt + 1]; ++e)
                 p->t_entries[fill[p->entries[e].kt]++] = NaEntry{(int32_t)qt, p->entries[e].mask};
     }
+    // ---- key/value tiles in pairs: merge the two ascending query-tile lists --
+    {
+        const int64_t npair = ceil_div(nkt, 2);
+        p->p_row_ptr.assign(npair + 1, 0);
+        p->p_entries.clear();
+        for (int64_t g = 0; g < npair; ++g) {
+            const int64_t ka = 2 * g, kb2 = 2 * g + 1;
+            int32_t a = p->t_row_ptr[ka], ae = p->t_row_ptr[ka + 1];
+            int32_t c = kb2 < nkt ? p->t_row_ptr[kb2] : 0, ce = kb2 < nkt ? p->t_row_ptr[kb2 + 1] : 0;
+            while (a < ae || c < ce) {
+                const int32_t qa = a < ae ? p->t_entries[a].kt : std::numeric_limits<int32_t>::max();
+                const int32_t qc = c < ce ? p->t_entries[c].kt : std::numeric_limits<int32_t>::max();
+                const int32_t qt = std::min(qa, qc);
+                NaPairEntry en{qt, NA_MASK_NONE, NA_MASK_NONE, 0};
+                if (qa == qt) en.mask0 = p->t_entries[a++].mask;
+                if (qc == qt) en.mask1 = p->t_entries[c++].mask;
+                p->p_entries.push_back(en);
+            }
+            p->p_row_ptr[g + 1] = (int32_t)p->p_entries.size();
+        }
+    }
     p->stats.n_tokens = N;
     p->stats.q_block = qb;
     p->stats.kv_block = kb;
