@@ -88,9 +88,10 @@ __global__ __launch_bounds__(256) void bwd_delta(NaBwdParams p) {
 //     P^T  = exp2(S^T scale log2 e - lse log2 e),  dS^T = P^T (dP^T - delta),
 //     dq^T += K^T dS^T                      (K^T by transposing LDS reads).
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, bool BIAS = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq(NaBwdParams p) {
+    using MaskT = typename MaskRow<BIAS>::T;
     constexpr int KV = NA_KV_BLOCK_BF16;
     constexpr int QB = 32 * NW;
     constexpr int ROW = D + 8;
@@ -139,7 +140,10 @@ void attn_bwd_dq(NaBwdParams p) {
             gf[s] = __builtin_bit_cast(bf16x8, x);
         }
     }
-    const float neg_lse2 = -lse_log2(qvalid ? p.lse[(int64_t)bh * N + qtok] : 0.f, qvalid);
+    // fixed fusion: the forward's lse carries log(alpha) (every logit's common
+    // prior); without it the window keys need no bias and the partners p.skip_bias
+    const float lse_raw = qvalid ? p.lse[(int64_t)bh * N + qtok] : 0.f;
+    const float neg_lse2 = -lse_log2(BIAS ? lse_raw - p.lse_shift : lse_raw, qvalid);
     const float dlt = qvalid ? p.delta[(int64_t)bh * N + qtok] : 0.f;
     const uint16_t* kbase = (const uint16_t*)p.k + b * p.k_sb + h * p.k_sh;
     const uint16_t* vbase = (const uint16_t*)p.v + b * p.v_sb + h * p.v_sh;
@@ -178,9 +182,18 @@ void attn_bwd_dq(NaBwdParams p) {
         }
     };
     auto mask_row = [&](NaEntry entry) {
-        u32x2 w = {0u, 0u};
-        if (entry.mask >= 0)
-            w = gload((const u32x2*)(p.masks + ((int64_t)entry.mask * QB + mrow) * 2));
+        MaskT w = {};
+        if (entry.mask >= 0) {
+            const int64_t at = ((int64_t)entry.mask * QB + mrow) * 2;
+            const u32x2 keep = gload((const u32x2*)(p.masks + at));
+            w[0] = keep[0];
+            w[1] = keep[1];
+            if constexpr (BIAS) {
+                const u32x2 part = gload((const u32x2*)(p.skip_masks + at));
+                w[2] = part[0];
+                w[3] = part[1];
+            }
+        }
         return w;
     };
 
@@ -195,7 +208,7 @@ void attn_bwd_dq(NaBwdParams p) {
     const int kappa = 16 * (l32 >> 4) + 2 * ((l32 >> 3) & 1) + ((l32 >> 2) & 1) + 4 * (l32 & 3);
     const int tr_base = (half + 4 * ((lane & 15) >> 2)) * ROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    auto compute = [&](NaEntry entry, u32x2 mk, const uint16_t* kl, const uint16_t* vl) {
+    auto compute = [&](NaEntry entry, MaskT mk, const uint16_t* kl, const uint16_t* vl) {
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = dp[0][r] = dp[1][r] = 0.f;
@@ -219,6 +232,15 @@ void attn_bwd_dq(NaBwdParams p) {
                 const int bit = 16 * (r / 8) + 2 * ((r / 4) % 2) + 4 * (r % 4);
                 s[0][r] = keep_if(w0, bit, s[0][r]);
                 s[1][r] = keep_if(w1, bit, s[1][r]);
+            }
+            if constexpr (BIAS) {
+                const uint32_t b0 = mk[2] >> half, b1 = mk[3] >> half;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int bit = 16 * (r / 8) + 2 * ((r / 4) % 2) + 4 * (r % 4);
+                    s[0][r] += ((b0 >> bit) & 1u) ? p.skip_bias : 0.f;
+                    s[1][r] += ((b1 >> bit) & 1u) ? p.skip_bias : 0.f;
+                }
             }
         }
         // P^T and dS^T in place of S^T
@@ -253,7 +275,7 @@ void attn_bwd_dq(NaBwdParams p) {
     const NaEntry none = {0, -1};
     NaEntry ent_a = none, ent_b = none, ent_c = none;
     int tok_n[IPW];
-    u32x2 mk_a = {0u, 0u}, mk_b = {0u, 0u};
+    MaskT mk_a = {}, mk_b = {};
     if (e0 < e1) {
         ent_a = load_entry(p.entries + e0);
         if (e0 + 1 < e1) ent_b = load_entry(p.entries + e0 + 1);
@@ -272,7 +294,7 @@ void attn_bwd_dq(NaBwdParams p) {
         __syncthreads();
         if (e + 1 < e1) issue(ent_b, tok_n, kn, vn);
         if (e + 2 < e1) tokens(ent_c, tok_n);
-        const u32x2 mk_c = e + 2 < e1 ? mask_row(ent_c) : u32x2{0u, 0u};
+        const MaskT mk_c = e + 2 < e1 ? mask_row(ent_c) : MaskT{};
         const NaEntry ent_d = e + 3 < e1 ? load_entry(p.entries + e + 3) : none;
         compute(ent_a, mk_a, kl, vl);
         ent_a = ent_b;
@@ -310,7 +332,7 @@ void attn_bwd_dq(NaBwdParams p) {
 // 16*(r/8) + 2*(r/4 % 2) + h + 4*(r%4) of the step; lse and delta are staged in
 // that order so that each lane reads its sixteen as four 16-byte words.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool BIAS = false>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))  // 192 / 294 registers
 void attn_bwd_dkdv(NaBwdParams p) {
@@ -326,7 +348,8 @@ void attn_bwd_dkdv(NaBwdParams p) {
     static_assert(2 * RSLOT % 64 == 0, "q and dout rows fill whole DMA blocks");
     constexpr int BPW = (NBLK + NW - 1) / NW;
     constexpr int RE = 2 * QS * ROW;             // LDS elements of a step's rows
-    constexpr int AUX = 2 * QS + 4 * QS;         // lse (log2), delta, mask words [2][QS][2]
+    // lse (log2), delta, mask words [2][QS][2] (and partner words [2][QS][2])
+    constexpr int AUX = 2 * QS + 4 * QS + (BIAS ? 4 * QS : 0);
 
     __shared__ __attribute__((aligned(1024))) uint16_t rows0[RE];
     __shared__ __attribute__((aligned(1024))) uint16_t rows1[RE];
@@ -442,17 +465,26 @@ void attn_bwd_dkdv(NaBwdParams p) {
         if (mask < 0) return 0u;
         return gload(p.masks + ((int64_t)mask * QBK + sb * QS + (lane >> 1)) * 2 + (lane & 1));
     };
-    auto aux_fetch = [&](Step st, float* lv, float* dl, uint32_t* mw0, uint32_t* mw1) {
+    auto part_word = [&](int mask, int sb) -> uint32_t {
+        if (mask < 0) return 0u;
+        return gload(p.skip_masks + ((int64_t)mask * QBK + sb * QS + (lane >> 1)) * 2 + (lane & 1));
+    };
+    auto aux_fetch = [&](Step st, float* lv, float* dl, u32x4* mw) {
         const int t = lane & 31;
         const int qp = st.qt * QBK + st.sb * QS + t;
         const bool valid = qp < N;
         const int tok = valid ? (p.perm ? gload(p.perm + qp) : qp) : 0;
-        *lv = lse_log2(valid ? gload(p.lse + (int64_t)bh * N + tok) : 0.f, valid);
+        const float lse = valid ? gload(p.lse + (int64_t)bh * N + tok) : 0.f;
+        *lv = lse_log2(BIAS ? lse - p.lse_shift : lse, valid);
         *dl = valid ? gload(p.delta + (int64_t)bh * N + tok) : 0.f;
-        *mw0 = mask_word(st.mask0, st.sb);
-        *mw1 = mask_word(st.mask1, st.sb);
+        (*mw)[0] = mask_word(st.mask0, st.sb);
+        (*mw)[1] = mask_word(st.mask1, st.sb);
+        if constexpr (BIAS) {
+            (*mw)[2] = part_word(st.mask0, st.sb);
+            (*mw)[3] = part_word(st.mask1, st.sb);
+        }
     };
-    auto aux_store = [&](float lv, float dl, uint32_t mw0, uint32_t mw1, float* aux) {
+    auto aux_store = [&](float lv, float dl, u32x4 mw, float* aux) {
         const int t = lane & 31;
         const int a = t >> 4, rem = t & 15;
         const int pos = 16 * (rem & 1) + 8 * a + 4 * ((rem >> 1) & 1) + (rem >> 2);
@@ -460,8 +492,12 @@ void attn_bwd_dkdv(NaBwdParams p) {
             aux[pos] = lv;
             aux[QS + pos] = dl;
         }
-        ((uint32_t*)aux)[2 * QS + lane] = mw0;
-        ((uint32_t*)aux)[4 * QS + lane] = mw1;
+        ((uint32_t*)aux)[2 * QS + lane] = mw[0];
+        ((uint32_t*)aux)[4 * QS + lane] = mw[1];
+        if constexpr (BIAS) {
+            ((uint32_t*)aux)[6 * QS + lane] = mw[2];
+            ((uint32_t*)aux)[8 * QS + lane] = mw[3];
+        }
     };
 
     const int kappa = 16 * (l32 >> 4) + 2 * ((l32 >> 3) & 1) + ((l32 >> 2) & 1) + 4 * (l32 & 3);
@@ -486,6 +522,7 @@ void attn_bwd_dkdv(NaBwdParams p) {
             }
         }
         const uint32_t* mrows = (const uint32_t*)aux + 2 * QS + (wave >= 2 ? 2 * QS : 0);
+        const uint32_t* prows = (const uint32_t*)aux + 6 * QS + (wave >= 2 ? 2 * QS : 0);
         const bool masked = my_mask >= 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -494,7 +531,14 @@ void attn_bwd_dkdv(NaBwdParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * i + j;
-                float pr = fast_exp2(__builtin_fmaf(s[r], c, -lv[j]));
+                float sr = s[r];
+                if constexpr (BIAS) {
+                    if (masked) {  // partners outside the window carry the extra log-prior
+                        const int q = 16 * (r / 8) + 2 * ((r / 4) % 2) + half + 4 * (r % 4);
+                        sr += (prows[2 * q + (wave & 1)] >> l32) & 1u ? p.skip_bias : 0.f;
+                    }
+                }
+                float pr = fast_exp2(__builtin_fmaf(sr, c, -lv[j]));
                 if (masked) {
                     const int q = 16 * (r / 8) + 2 * ((r / 4) % 2) + half + 4 * (r % 4);
                     pr = (mrows[2 * q + (wave & 1)] >> l32) & 1u ? pr : 0.f;
@@ -536,10 +580,10 @@ void attn_bwd_dkdv(NaBwdParams p) {
         tokens(cur, tok);
         issue(tok, rows0);
         float lv, dl;
-        uint32_t mw0, mw1;
+        u32x4 mw = {0u, 0u, 0u, 0u};
         if (wave == 0) {
-            aux_fetch(cur, &lv, &dl, &mw0, &mw1);
-            aux_store(lv, dl, mw0, mw1, aux0);
+            aux_fetch(cur, &lv, &dl, &mw);
+            aux_store(lv, dl, mw, aux0);
         }
         int tok_n[BPW];
         if (nx.e < t1) tokens(nx, tok_n);
@@ -549,11 +593,11 @@ void attn_bwd_dkdv(NaBwdParams p) {
             const Step nn = nx.e < t1 ? next_step(nx) : nx;
             if (nx.e < t1) {
                 issue(tok_n, rn);
-                if (wave == 0) aux_fetch(nx, &lv, &dl, &mw0, &mw1);
+                if (wave == 0) aux_fetch(nx, &lv, &dl, &mw);
                 if (nn.e < t1) tokens(nn, tok_n);
             }
             compute(cur, rl, al);
-            if (nx.e < t1 && wave == 0) aux_store(lv, dl, mw0, mw1, an);
+            if (nx.e < t1 && wave == 0) aux_store(lv, dl, mw, an);
             cur = nx;
             nx = nn;
         };
@@ -578,29 +622,28 @@ bool na_bwd_supported(int dtype, int head_dim, int q_block, int kv_block) {
            (q_block == 128 || q_block == 256);
 }
 
-int na_bwd_launch(const NaBwdParams& p, int head_dim, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
+namespace {
+
+template <int D, bool BIAS>
+int launch_bwd(const NaBwdParams& p, hipStream_t st) {
     const int64_t rows = (int64_t)p.batch * p.heads * p.n_tokens;
-    const int lanes = head_dim / 8;
-    const dim3 gd((unsigned)((rows * lanes + 255) / 256));
+    const dim3 gd((unsigned)((rows * (D / 8) + 255) / 256));
     const dim3 gq((unsigned)((int64_t)p.n_q_tiles * p.batch * p.heads));
     const dim3 gk((unsigned)((int64_t)((p.n_kv_tiles + 1) / 2) * p.batch * p.heads));
-    if (head_dim == 128) {
-        hipLaunchKernelGGL((bwd_delta<128>), gd, dim3(256), 0, st, p);
-        if (p.q_block == 256)
-            hipLaunchKernelGGL((attn_bwd_dq<128, 8>), gq, dim3(512), 0, st, p);
-        else
-            hipLaunchKernelGGL((attn_bwd_dq<128, 4>), gq, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((attn_bwd_dkdv<128>), gk, dim3(256), 0, st, p);
-    } else if (head_dim == 64) {
-        hipLaunchKernelGGL((bwd_delta<64>), gd, dim3(256), 0, st, p);
-        if (p.q_block == 256)
-            hipLaunchKernelGGL((attn_bwd_dq<64, 8>), gq, dim3(512), 0, st, p);
-        else
-            hipLaunchKernelGGL((attn_bwd_dq<64, 4>), gq, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((attn_bwd_dkdv<64>), gk, dim3(256), 0, st, p);
-    } else {
-        return (int)hipErrorInvalidValue;
-    }
+    hipLaunchKernelGGL((bwd_delta<D>), gd, dim3(256), 0, st, p);
+    if (p.q_block == 256)
+        hipLaunchKernelGGL((attn_bwd_dq<D, 8, BIAS>), gq, dim3(512), 0, st, p);
+    else
+        hipLaunchKernelGGL((attn_bwd_dq<D, 4, BIAS>), gq, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv<D, BIAS>), gk, dim3(256), 0, st, p);
     return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int na_bwd_launch(const NaBwdParams& p, int head_dim, bool fusion, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (head_dim == 128) return fusion ? launch_bwd<128, true>(p, st) : launch_bwd<128, false>(p, st);
+    if (head_dim == 64) return fusion ? launch_bwd<64, true>(p, st) : launch_bwd<64, false>(p, st);
+    return (int)hipErrorInvalidValue;
 }

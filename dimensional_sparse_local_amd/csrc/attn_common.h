@@ -54,6 +54,11 @@ __device__ __forceinline__ NaEntry load_entry(const NaEntry* e) {
     return NaEntry{v[0], v[1]};
 }
 
+// Mask words of one query row for one tile: the keep plane (2 words), and with
+// BIAS the partner plane of fixed fusion (2 more words).
+template <bool BIAS> struct MaskRow { using T = u32x2; };
+template <> struct MaskRow<true> { using T = u32x4; };
+
 // Keep score x when bit `bit` of word w is set, else -inf.
 __device__ __forceinline__ float keep_if(uint32_t w, int bit, float x) {
     return (w >> bit) & 1u ? x : kNegInf;

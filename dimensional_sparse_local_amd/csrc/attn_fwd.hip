@@ -48,11 +48,6 @@ namespace {
 // by more than 2^8, which keeps every P <= 256 and is exact after the final
 // division by l.
 // ---------------------------------------------------------------------------
-// Mask words of one query row for one tile: the keep plane (2 words), and with
-// BIAS the partner plane of fixed fusion (2 more words).
-template <bool BIAS> struct MaskRow { using T = u32x2; };
-template <> struct MaskRow<true> { using T = u32x4; };
-
 template <int D, int NW, bool BIAS = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : 2, NW > 8 ? 3 : 2)))

@@ -431,11 +431,12 @@ na_status na_backward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, con
         return NA_ERR_INVALID_ARG;
     }
     const na_plan_desc& d = p->desc;
-    if (d.skip > 0 && d.skip_mode != NA_SKIP_UNION) {
-        na_set_error("gradients of the fixed-fusion and separate-softmax variants are not built "
-                     "(the union form is)");
+    if (d.skip > 0 && d.skip_mode == NA_SKIP_SEPARATE) {
+        na_set_error("gradients of the separate-softmax variant are not built (the union and "
+                     "fixed-fusion forms are)");
         return NA_ERR_UNSUPPORTED;
     }
+    const bool fusion = d.skip > 0 && d.skip_mode == NA_SKIP_FIXED_FUSION;
     if (!na_bwd_supported(d.dtype, d.head_dim, d.q_block, d.kv_block)) {
         na_set_error("no gradient kernels for dtype=%d head_dim=%d q_block=%d kv_block=%d",
                      d.dtype, d.head_dim, d.q_block, d.kv_block);
@@ -481,8 +482,14 @@ na_status na_backward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, con
     a.p_entries = p->d_p_entries;
     a.masks = p->d_masks;
     a.zero = p->d_zero;
+    if (fusion) {  // the forward's logit bias and lse shift (see na_forward)
+        const double alpha = d.skip_prior;
+        a.skip_masks = p->d_skip_masks;
+        a.skip_bias = (float)(std::log((1.0 - alpha) / alpha) / (double)scale);
+        a.lse_shift = (float)std::log(alpha);
+    }
     if (p->n_tokens == 0) return NA_OK;
-    const int rc = na_bwd_launch(a, d.head_dim, stream);
+    const int rc = na_bwd_launch(a, d.head_dim, fusion, stream);
     if (rc != 0) {
         na_set_error("kernel launch failed: %s", hip_err((hipError_t)rc));
         return NA_ERR_DEVICE;

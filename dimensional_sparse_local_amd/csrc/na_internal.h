@@ -158,12 +158,18 @@ struct NaBwdParams {
     const NaPairEntry* p_entries;
     const uint32_t* masks;
     const void* zero;      // >= 1 KiB of zeros
+    // fixed fusion only (as in NaAttnParams): partner planes, the partners'
+    // raw dot-product bias and the log(alpha) the forward added to lse
+    const uint32_t* skip_masks;
+    float skip_bias;
+    float lse_shift;
 };
 
 // Returns false if no gradient kernels exist for (dtype, head_dim, q_block, kv_block).
 bool na_bwd_supported(int dtype, int head_dim, int q_block, int kv_block);
 // Launch the three gradient kernels (row sums, dq, dk/dv); HIP error code.
-int na_bwd_launch(const NaBwdParams& p, int head_dim, void* stream);
+// fusion = the fixed-fusion (logit bias) variants.
+int na_bwd_launch(const NaBwdParams& p, int head_dim, bool fusion, void* stream);
 
 // Returns false if no variant exists for (dtype, head_dim, q_block, kv_block);
 // fusion = the fixed-fusion (logit bias) variant.
