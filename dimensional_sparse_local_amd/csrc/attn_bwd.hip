@@ -625,12 +625,12 @@ bool na_bwd_supported(int dtype, int head_dim, int q_block, int kv_block) {
 namespace {
 
 template <int D, bool BIAS>
-int launch_bwd(const NaBwdParams& p, hipStream_t st) {
+int launch_bwd(const NaBwdParams& p, bool with_delta, hipStream_t st) {
     const int64_t rows = (int64_t)p.batch * p.heads * p.n_tokens;
     const dim3 gd((unsigned)((rows * (D / 8) + 255) / 256));
     const dim3 gq((unsigned)((int64_t)p.n_q_tiles * p.batch * p.heads));
     const dim3 gk((unsigned)((int64_t)((p.n_kv_tiles + 1) / 2) * p.batch * p.heads));
-    hipLaunchKernelGGL((bwd_delta<D>), gd, dim3(256), 0, st, p);
+    if (with_delta) hipLaunchKernelGGL((bwd_delta<D>), gd, dim3(256), 0, st, p);
     if (p.q_block == 256)
         hipLaunchKernelGGL((attn_bwd_dq<D, 8, BIAS>), gq, dim3(512), 0, st, p);
     else
@@ -641,9 +641,11 @@ int launch_bwd(const NaBwdParams& p, hipStream_t st) {
 
 }  // namespace
 
-int na_bwd_launch(const NaBwdParams& p, int head_dim, bool fusion, void* stream) {
+int na_bwd_launch(const NaBwdParams& p, int head_dim, bool fusion, bool with_delta, void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    if (head_dim == 128) return fusion ? launch_bwd<128, true>(p, st) : launch_bwd<128, false>(p, st);
-    if (head_dim == 64) return fusion ? launch_bwd<64, true>(p, st) : launch_bwd<64, false>(p, st);
+    if (head_dim == 128)
+        return fusion ? launch_bwd<128, true>(p, with_delta, st) : launch_bwd<128, false>(p, with_delta, st);
+    if (head_dim == 64)
+        return fusion ? launch_bwd<64, true>(p, with_delta, st) : launch_bwd<64, false>(p, with_delta, st);
     return (int)hipErrorInvalidValue;
 }

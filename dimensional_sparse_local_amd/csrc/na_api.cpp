@@ -431,12 +431,8 @@ na_status na_backward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, con
         return NA_ERR_INVALID_ARG;
     }
     const na_plan_desc& d = p->desc;
-    if (d.skip > 0 && d.skip_mode == NA_SKIP_SEPARATE) {
-        na_set_error("gradients of the separate-softmax variant are not built (the union and "
-                     "fixed-fusion forms are)");
-        return NA_ERR_UNSUPPORTED;
-    }
     const bool fusion = d.skip > 0 && d.skip_mode == NA_SKIP_FIXED_FUSION;
+    const bool separate = d.skip > 0 && d.skip_mode == NA_SKIP_SEPARATE;
     if (!na_bwd_supported(d.dtype, d.head_dim, d.q_block, d.kv_block)) {
         na_set_error("no gradient kernels for dtype=%d head_dim=%d q_block=%d kv_block=%d",
                      d.dtype, d.head_dim, d.q_block, d.kv_block);
@@ -488,8 +484,19 @@ na_status na_backward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, con
         a.skip_bias = (float)(std::log((1.0 - alpha) / alpha) / (double)scale);
         a.lse_shift = (float)std::log(alpha);
     }
+    a.skip = d.skip;
+    a.skip_both = d.skip_both;
     if (p->n_tokens == 0) return NA_OK;
-    const int rc = na_bwd_launch(a, d.head_dim, fusion, stream);
+    int rc = 0;
+    if (separate) {
+        // the window branch over the plan's (window-only) map with the window
+        // branch's own row sums, then the partner branch's gradients added
+        rc = na_skip_bwd_delta_launch(a, d.head_dim, stream);
+        if (rc == 0) rc = na_bwd_launch(a, d.head_dim, false, false, stream);
+        if (rc == 0) rc = na_skip_bwd_grads_launch(a, d.head_dim, stream);
+    } else {
+        rc = na_bwd_launch(a, d.head_dim, fusion, true, stream);
+    }
     if (rc != 0) {
         na_set_error("kernel launch failed: %s", hip_err((hipError_t)rc));
         return NA_ERR_DEVICE;

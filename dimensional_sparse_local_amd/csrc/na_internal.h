@@ -163,13 +163,17 @@ struct NaBwdParams {
     const uint32_t* skip_masks;
     float skip_bias;
     float lse_shift;
+    // separate-softmax partners (pi_skip.hip): x - skip (and x + skip)
+    int32_t skip;
+    int32_t skip_both;
 };
 
 // Returns false if no gradient kernels exist for (dtype, head_dim, q_block, kv_block).
 bool na_bwd_supported(int dtype, int head_dim, int q_block, int kv_block);
 // Launch the three gradient kernels (row sums, dq, dk/dv); HIP error code.
-// fusion = the fixed-fusion (logit bias) variants.
-int na_bwd_launch(const NaBwdParams& p, int head_dim, bool fusion, void* stream);
+// fusion = the fixed-fusion (logit bias) variants; with_delta = false skips the
+// row sums (the caller has written p.delta).
+int na_bwd_launch(const NaBwdParams& p, int head_dim, bool fusion, bool with_delta, void* stream);
 
 // Returns false if no variant exists for (dtype, head_dim, q_block, kv_block);
 // fusion = the fixed-fusion (logit bias) variant.
@@ -199,6 +203,11 @@ struct NaSkipParams {
 };
 bool na_skip_supported(int dtype, int head_dim);
 int na_skip_launch(const NaSkipParams& p, int dtype, int head_dim, void* stream);
+// Gradients of the separate-softmax variant (bf16): delta_i of the window
+// branch alone (before the gradient kernels, in place of their row sums), and
+// the partner branch's dq, dk, dv added to theirs (after).
+int na_skip_bwd_delta_launch(const NaBwdParams& p, int head_dim, void* stream);
+int na_skip_bwd_grads_launch(const NaBwdParams& p, int head_dim, void* stream);
 
 // Row gather / scatter (permute.hip): rows of row_bytes bytes (a multiple of 4);
 // all strides in bytes.

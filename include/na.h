@@ -232,10 +232,12 @@ size_t na_backward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H);
  * must not overlap the inputs.  workspace: >= na_backward_workspace_bytes,
  * 256-byte aligned, caller-owned; no allocation happens.  bf16 only, head_dim
  * 64 or 128, (q_block, kv_block) = (128, 64) or (256, 64); other plans return
- * NA_ERR_UNSUPPORTED, and so do plans with a skip partner in the separate-
- * softmax mode (the union mode is an ordinary neighbourhood; fixed fusion adds
- * its constant log-priors to the recomputed logits, which leaves the softmax
- * Jacobian unchanged).  P and dS are rounded to bf16 before their MFMA
+ * NA_ERR_UNSUPPORTED.  With a skip partner: the union mode is an ordinary
+ * neighbourhood; fixed fusion adds its constant log-priors to the recomputed
+ * logits (the softmax Jacobian is unchanged); the separate-softmax mode
+ * computes the window branch's gradients with that branch's own row sums and
+ * adds the partner branch's (two more kernels; lse is the window branch's, as
+ * na_forward returns it).  P and dS are rounded to bf16 before their MFMA
  * products, accumulation is fp32.  Asynchronous on stream. */
 na_status na_backward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
                       const na_tensor* k, const na_tensor* v, const na_tensor* out,

@@ -142,13 +142,20 @@ GRAD_CASES = [
     (_pi("g_fusion_near", N=500, left=20, right=0, skip=7, mode="fixed_fusion", prior=0.2), 256),
     (_pi("g_fusion_hilbert", left=10, right=10, skip=100, both=1, mode="fixed_fusion", prior=0.3,
          hilbert=32), 128),
+    (_pi("g_separate", N=600, left=6, right=0, skip=50, mode="separate"), 0),
+    (_pi("g_separate_both", N=700, left=8, right=8, skip=40, both=1, mode="separate", D=128), 256),
+    (_pi("g_separate_near", N=500, left=20, right=0, skip=7, both=1, mode="separate"), 128),
+    (_pi("g_separate_hilbert", left=10, right=10, skip=100, both=1, mode="separate", hilbert=32),
+     128),
 ]
 
 
 @pytest.mark.parametrize("wl,q_block", GRAD_CASES, ids=[w["name"] for w, _ in GRAD_CASES])
 def test_pi_gradients(wl, q_block):
     """The union form is an ordinary neighbourhood; fixed fusion's log-priors are
-    constants added to the recomputed logits (same kernels, a partner bit plane)."""
+    constants added to the recomputed logits (same kernels, a partner bit plane);
+    the separate variant adds the partner branch's gradients to the window
+    branch's, whose row sums use the window output alone."""
     na = _na()
     print("case %s q_block=%d" % (wl["name"], q_block), flush=True)
     plan = na.Plan(wl, q_block=q_block)
@@ -164,16 +171,3 @@ def test_pi_gradients(wl, q_block):
         rel = np.linalg.norm(a - want) / np.linalg.norm(want)
         mx = np.max(np.abs(a - want)) / np.max(np.abs(want))
         assert rel <= 1e-2 and mx <= 2e-2, "%s %s rel-L2 %.3e max %.3e" % (wl["name"], name, rel, mx)
-
-
-def test_pi_separate_gradients_unsupported():
-    na = _na()
-    for mode in ("separate",):
-        wl = _pi("g_" + mode, N=300, mode=mode, prior=0.3)
-        plan = na.Plan(wl)
-        q, k, v = W.make_qkv(wl, device="cuda")
-        out, lse = plan.forward(q, k, v, scale=0.125)
-        with pytest.raises(na.NaError) as ei:
-            plan.backward(q, k, v, out, lse, out, scale=0.125)
-        assert ei.value.status == na.NA_ERR_UNSUPPORTED
-    torch.cuda.synchronize()
