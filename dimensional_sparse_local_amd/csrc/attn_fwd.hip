@@ -23,7 +23,9 @@ namespace {
 // bf16: NW waves of 32 queries each (query tile 32*NW), key/value tile 64.
 //
 // Two waves share every SIMD (<= 256 registers each), so the MFMA phase of one
-// overlaps the softmax phase of the other.  With 12 waves (384 queries: one
+// overlaps the softmax phase of the other.  At D = 64 (128 registers) four
+// waves share a SIMD, so up to four workgroups per CU keep K/V requests in
+// flight for the short CSR rows of small windows.  With 12 waves (384 queries: one
 // 6x8x8 sliding tile) three waves share a SIMD (<= 168 registers): each K/V
 // tile staged from L2 then serves 1.5 times the queries, which is what limits
 // these kernels (staging the tiles, not the barriers or the waits, costs about
@@ -50,7 +52,8 @@ namespace {
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool BIAS = false>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : 2, NW > 8 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : (D == 64 && NW >= 4 && !BIAS ? 4 : 2),
+                                   NW > 8 ? 3 : (D == 64 && NW >= 4 && !BIAS ? 4 : 2))))
 void attn_fwd_bf16(NaAttnParams p) {
     using MaskT = typename MaskRow<BIAS>::T;
     constexpr int KV = NA_KV_BLOCK_BF16;
