@@ -334,7 +334,7 @@ void attn_bwd_dq(NaBwdParams p) {
 // ---------------------------------------------------------------------------
 template <int D, bool BIAS = false>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))  // 192 / 294 registers
+__attribute__((amdgpu_waves_per_eu(2, 2)))   // two waves per SIMD: <= 256 registers
 void attn_bwd_dkdv(NaBwdParams p) {
     constexpr int KV = NA_KV_BLOCK_BF16;
     constexpr int NW = 4;
@@ -376,7 +376,11 @@ void attn_bwd_dkdv(NaBwdParams p) {
     const int kpos = kg * 2 * KV + 32 * wave + l32;   // waves 0-1: tile 2 kg, 2-3: 2 kg + 1
     const bool kvalid = kpos < N;
     const int ktok = kvalid ? (p.perm ? p.perm[kpos] : kpos) : 0;
-    bf16x8 kf[KS], vf[KS];
+    bf16x8 kf[KS];
+    // The V fragments wait in LDS (each lane reads back its own 16-byte words,
+    // one read per dP MFMA): 32 registers fewer, which lets two waves share a
+    // SIMD and hide each other's LDS and softmax latency.
+    __shared__ __attribute__((aligned(16))) u32x4 vfrag[NW * KS * 64];
     {
         const uint16_t* krow = (const uint16_t*)p.k + b * p.k_sb + h * p.k_sh + (int64_t)ktok * p.k_sn;
         const uint16_t* vrow = (const uint16_t*)p.v + b * p.v_sb + h * p.v_sh + (int64_t)ktok * p.v_sn;
@@ -388,7 +392,7 @@ void attn_bwd_dkdv(NaBwdParams p) {
                 x = *(const u32x4*)(vrow + 16 * s + 8 * half);
             }
             kf[s] = __builtin_bit_cast(bf16x8, w);
-            vf[s] = __builtin_bit_cast(bf16x8, x);
+            vfrag[(wave * KS + s) * 64 + lane] = x;
         }
     }
     const uint16_t* qbase = (const uint16_t*)p.q + b * p.q_sb + h * p.q_sh;
@@ -517,7 +521,8 @@ void attn_bwd_dkdv(NaBwdParams p) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qr + 16 * ks), kf[ks], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(gr + 16 * ks), vf[ks], dp, 0,
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(gr + 16 * ks),
+                                                             __builtin_bit_cast(bf16x8, vfrag[(wave * KS + ks) * 64 + lane]), dp, 0,
                                                              0, 0);
             }
         }
