@@ -189,3 +189,19 @@ GNA = [
 @pytest.mark.parametrize("wl", GNA, ids=[w["name"] for w in GNA])
 def test_backward_gna(wl, q_block):
     _grad_case(wl, q_block=q_block)
+
+
+def test_backward_unsupported_query_tiles():
+    """Gradient kernels exist for 128- and 256-query tiles: plans built with 64
+    (head_dim 64) or 384 (head_dim 128) query tiles refuse na_backward."""
+    na = _na()
+    for D, qb in ((64, 64), (128, 384)):
+        wl = W.scaled(W.CONFIGS["causal1d_bf16"], name="qb%d" % qb, H=1, D=D, grid=[500],
+                      pattern=dict(kind="band", left=40, right=0))
+        plan = na.Plan(wl, q_block=qb)
+        q, k, v = W.make_qkv(wl, device="cuda")
+        out, lse = plan.forward(q, k, v, scale=0.1)
+        with pytest.raises(na.NaError) as ei:
+            plan.backward(q, k, v, out, lse, out, scale=0.1)
+        assert ei.value.status == na.NA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()

@@ -171,3 +171,15 @@ def test_pi_gradients(wl, q_block):
         rel = np.linalg.norm(a - want) / np.linalg.norm(want)
         mx = np.max(np.abs(a - want)) / np.max(np.abs(want))
         assert rel <= 1e-2 and mx <= 2e-2, "%s %s rel-L2 %.3e max %.3e" % (wl["name"], name, rel, mx)
+
+
+@pytest.mark.parametrize("q_block,D", [(192, 64), (384, 128)])
+def test_pi_fixed_fusion_unsupported_tiles(q_block, D):
+    """The logit-bias forward exists for 64 (head_dim 64), 128 and 256 query tiles."""
+    na = _na()
+    wl = _pi("fusion_qb%d" % q_block, N=500, mode="fixed_fusion", prior=0.3, D=D)
+    plan = na.Plan(wl, q_block=q_block)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    with pytest.raises(na.NaError) as ei:
+        plan.forward(q, k, v, scale=0.125)
+    assert ei.value.status == na.NA_ERR_UNSUPPORTED
