@@ -86,9 +86,18 @@ def cpu_baseline(wl, q, k, v, scale, target_s: float):
     count = int(min(n, max(c, target_s / max(per_row, 1e-9))))
     dt, pairs, c = run(count)
     flops = 4.0 * int(wl["D"]) * pairs
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d query rows of batch 0, head 0 (%.3g effective flops) in %.1f s, fp64, "
-                      "OpenMP" % (c, flops, dt)}
+                      "OpenMP, %d threads on %s" % (c, flops, dt, threads, model)}
 
 
 def main():
