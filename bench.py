@@ -156,10 +156,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q_block = args.q_block
+    internal = None
     if q_block == 0 and args.which == "forward" and D == 128 and wl["dtype"] == "bf16":
         if na.Plan(wl, host_only=True, q_block=384).stats["n_partial"] == 0:
             q_block = 384
-    plan = na.Plan(wl, q_block=q_block)
+    if (q_block == 0 and args.which == "forward" and D == 64 and wl["dtype"] == "bf16"
+            and wl["order"] == "row_major" and len(wl["grid"]) == 2
+            and wl["pattern"]["kind"] in ("na", "sa")):
+        # the token order inside the kernel is free (q, k, v, out stay row-major):
+        # 8x8 patches make the visited tile pairs denser, 64-query tiles give
+        # the short walks more workgroups
+        internal = dict(order="tiled", tile=[8, 8])
+        q_block = 64
+    plan = na.Plan(W.scaled(wl, **internal) if internal else wl, q_block=q_block)
     flops = plan.effective_flops(B, H)
     q, k, v = W.make_qkv(wl, device=dev)
     scale = W.default_scale(wl)
@@ -279,7 +288,8 @@ def main():
                    "attended_pairs_per_head": plan.stats["attended_pairs"],
                    "effective_flops_per_step": flops,
                    "pct_of_peak": round(100.0 * tflops / peak, 2),
-                   "permute_passes": bool(args.permute_passes), "pass": args.which},
+                   "permute_passes": bool(args.permute_passes), "pass": args.which,
+                   "internal_order": internal or {"order": wl["order"]}},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -372,3 +372,11 @@ Q64 = [w for w in SMALL_BF16 if w["D"] == 64] + [
 @pytest.mark.parametrize("wl", Q64, ids=[w["name"] for w in Q64])
 def test_query_block_64(wl):
     _run(wl, q_block=64)
+
+
+def test_full_size_na2d_as_benched():
+    """The 64x64 13x13 neighbourhood workload as the benchmark launches its
+    forward pass: 8x8 patch order inside the kernel, 64-query tiles, every
+    element compared (inputs and outputs stay in row-major order)."""
+    wl = W.scaled(W.CONFIGS["na2d_bf16"], order="tiled", tile=[8, 8])
+    _run(wl, q_block=64)
