@@ -322,3 +322,14 @@ def test_pi_fixed_fusion_needs_prior_in_open_interval(prior):
     with pytest.raises(na.NaError) as ei:
         na.Plan(d, host_only=True)
     assert ei.value.status == na.NA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", [n for n in list(W.HILBERT_PAGE) + list(W.GNA) + list(W.PI_ATTENTION)
+                                  if n != "sta3d_causal_t_bf16"])
+def test_named_workload_tile_maps(name):
+    """Every named workload's tile map (classes, pair counts, order) equals the
+    oracle's at the library's default tiles and at 64-query tiles."""
+    wl = W.ALL[name]
+    p = na.Plan(wl, host_only=True)
+    _compare(wl, p.stats["q_block"], p.stats["kv_block"])
+    _compare(wl, 64, 64)
