@@ -16,6 +16,7 @@
 // Local Attention", methodology).
 
 #include "attn_common.h"
+#include <type_traits>
 
 namespace {
 
@@ -194,7 +195,17 @@ void attn_fwd_bf16(NaAttnParams p) {
     // 32*db + 16*(g%2) + 4*(s%4).
     const int tr_base = (half + 4 * ((lane & 15) >> 2)) * ROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+    // With three waves per SIMD, a wave in an MFMA phase takes issue priority so
+    // that the others' softmax work fills the gaps instead of competing for the
+    // MFMA pipe (measured: 2 % on 384-query tiles; with two waves it costs 2 %).
+    auto mfma_phase = [&](auto on) {
+        if constexpr (NW > 8) {
+            if constexpr (decltype(on)::value) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
+    };
     auto compute = [&](NaEntry entry, MaskT mk, const uint16_t* kl, const uint16_t* vl) {
+        mfma_phase(std::true_type{});
         // S^T = K Q^T for the two 32-key halves of the tile.  All KS fragments
         // of the first half are requested up front; each MFMA of the first
         // half is then followed by the request for the matching fragment of
@@ -236,6 +247,7 @@ void attn_fwd_bf16(NaAttnParams p) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);   // KS MFMAs
         }
+        mfma_phase(std::false_type{});
         // element mask (partial tiles and tiles past the last key only): score
         // (kb, r) is key 32*kb + 16*(r/8) + 2*(r/4 % 2) + half + 4*(r % 4)
         if (entry.mask >= 0) {
@@ -282,6 +294,7 @@ void attn_fwd_bf16(NaAttnParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+        mfma_phase(std::true_type{});
         // O^T += V^T P^T, 16 keys per step.  Step ks covers accumulator
         // elements r0 = 8*(ks%2) .. r0+7 of score block ks/2: slot e of half h
         // is key 16*ks + 2*(e/4) + h + 4*(e%4), the row the transpose reads
@@ -303,6 +316,7 @@ void attn_fwd_bf16(NaAttnParams p) {
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[db], 0, 0, 0);
             }
         }
+        mfma_phase(std::false_type{});
     };
 
     // ---- pipelined walk over the CSR row ------------------------------------
