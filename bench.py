@@ -77,8 +77,13 @@ def cpu_baseline(wl, q, k, v, scale, target_s: float):
         t0 = time.perf_counter()
         oracle.attention(wl, q1, k1, v1, scale, rows=rows)
         dt = time.perf_counter() - t0
-        pairs = sum(len(oracle.neighbors(wl, int(r))) for r in rows[: min(len(rows), 64)])
-        pairs = pairs * len(rows) / min(len(rows), 64)
+        if len(rows) == n:
+            pairs = oracle.attended_pairs(wl)   # every row: the exact count
+        else:
+            # rows differ in their key counts (borders, causal starts): estimate
+            # from a uniform subset of the sample, not from its first rows
+            sub = rng.choice(rows, size=min(len(rows), 256), replace=False)
+            pairs = sum(len(oracle.neighbors(wl, int(r))) for r in sub) * len(rows) / len(sub)
         return dt, pairs, len(rows)
 
     dt, _, c = run(min(n, 4 * threads))
