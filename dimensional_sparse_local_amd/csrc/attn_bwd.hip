@@ -181,18 +181,21 @@ void attn_bwd_dq(NaBwdParams p) {
             }
         }
     };
+    // The mask row is loaded unconditionally (the zero page stands in for a
+    // tile without a mask, whose words are never read): a load merged with a
+    // constant would be consumed at once, and that wait would also cover the
+    // K/V rows just sent to LDS.
     auto mask_row = [&](NaEntry entry) {
-        MaskT w = {};
-        if (entry.mask >= 0) {
-            const int64_t at = ((int64_t)entry.mask * QB + mrow) * 2;
-            const u32x2 keep = gload((const u32x2*)(p.masks + at));
-            w[0] = keep[0];
-            w[1] = keep[1];
-            if constexpr (BIAS) {
-                const u32x2 part = gload((const u32x2*)(p.skip_masks + at));
-                w[2] = part[0];
-                w[3] = part[1];
-            }
+        MaskT w;
+        const int64_t at = ((int64_t)entry.mask * QB + mrow) * 2;
+        const bool has = entry.mask >= 0;
+        const u32x2 keep = gload((const u32x2*)(has ? p.masks + at : (const uint32_t*)p.zero));
+        w[0] = keep[0];
+        w[1] = keep[1];
+        if constexpr (BIAS) {
+            const u32x2 part = gload((const u32x2*)(has ? p.skip_masks + at : (const uint32_t*)p.zero));
+            w[2] = part[0];
+            w[3] = part[1];
         }
         return w;
     };
@@ -294,7 +297,7 @@ void attn_bwd_dq(NaBwdParams p) {
         __syncthreads();
         if (e + 1 < e1) issue(ent_b, tok_n, kn, vn);
         if (e + 2 < e1) tokens(ent_c, tok_n);
-        const MaskT mk_c = e + 2 < e1 ? mask_row(ent_c) : MaskT{};
+        const MaskT mk_c = mask_row(ent_c);   // ent_c is `none` past the row's end
         const NaEntry ent_d = e + 3 < e1 ? load_entry(p.entries + e + 3) : none;
         compute(ent_a, mk_a, kl, vl);
         ent_a = ent_b;
@@ -322,8 +325,8 @@ void attn_bwd_dq(NaBwdParams p) {
 // staging their q and dout rows in LDS by DMA (double-buffered, the next step
 // in flight) together with their lse, delta and the mask words of both tiles.
 // Staging one step for 128 keys instead of 64 halves the staged bytes per
-// flop, which is what bounds this kernel.  A wave whose tile the step's query
-// tile does not attend skips the step's arithmetic.  Per step, with the roles of the forward swapped
+// flop.  A wave whose tile the step's query tile does not attend skips the
+// step's arithmetic.  Per step, with the roles of the forward swapped
 // (lane = key, q / dout rows permuted inside the MFMA block):
 //     S = Q K^T,  dP = dout V^T               (q and dout rows as A operands),
 //     P = exp2(S scale log2 e - lse log2 e),  dS = P (dP - delta),
@@ -459,45 +462,49 @@ void attn_bwd_dkdv(NaBwdParams p) {
             }
         }
     };
-    // lse / delta / mask words of a step, fetched into registers by wave 0 and
-    // written to LDS at the end of the previous step: lane t < 32 holds query t
-    // (stored at the accumulator position of query t), lane l holds mask word
-    // (row l / 2, word l % 2) of each tile: all ones for a tile without a mask,
-    // zero for a tile the query tile does not attend.
-    auto mask_word = [&](int mask, int sb) -> uint32_t {
-        if (mask == -1) return ~0u;
-        if (mask < 0) return 0u;
-        return gload(p.masks + ((int64_t)mask * QBK + sb * QS + (lane >> 1)) * 2 + (lane & 1));
+    // lse / delta / mask words of a step, loaded into registers by wave 0 one
+    // step ahead and written to LDS at the end of the previous step: lane t < 32
+    // holds query t (stored at the accumulator position of query t), lane l
+    // holds mask word (row l / 2, word l % 2) of each tile: all ones for a tile
+    // without a mask, zero for a tile the query tile does not attend.  The
+    // loads are unconditional from always-valid addresses (the query's token
+    // clamped to the last one, fetched a step earlier still; the zero page for
+    // tiles without a mask word) and every select waits for the store, after
+    // the step's compute: a use right after a load would make wave 0 wait for
+    // the rows just sent to LDS as well (the wait counter is in order).
+    auto mask_src = [&](int mask, int sb) -> const uint32_t* {
+        return mask >= 0 ? p.masks + ((int64_t)mask * QBK + sb * QS) * 2 : (const uint32_t*)p.zero;
     };
-    auto part_word = [&](int mask, int sb) -> uint32_t {
-        if (mask < 0) return 0u;
-        return gload(p.skip_masks + ((int64_t)mask * QBK + sb * QS + (lane >> 1)) * 2 + (lane & 1));
+    auto part_src = [&](int mask, int sb) -> const uint32_t* {
+        return mask >= 0 ? p.skip_masks + ((int64_t)mask * QBK + sb * QS) * 2 : (const uint32_t*)p.zero;
     };
-    auto aux_fetch = [&](Step st, float* lv, float* dl, u32x4* mw) {
-        const int t = lane & 31;
-        const int qp = st.qt * QBK + st.sb * QS + t;
-        const bool valid = qp < N;
-        const int tok = valid ? (p.perm ? gload(p.perm + qp) : qp) : 0;
-        const float lse = valid ? gload(p.lse + (int64_t)bh * N + tok) : 0.f;
-        *lv = lse_log2(BIAS ? lse - p.lse_shift : lse, valid);
-        *dl = valid ? gload(p.delta + (int64_t)bh * N + tok) : 0.f;
-        (*mw)[0] = mask_word(st.mask0, st.sb);
-        (*mw)[1] = mask_word(st.mask1, st.sb);
+    auto aux_valid = [&](Step st) { return st.qt * QBK + st.sb * QS + (lane & 31) < N; };
+    auto aux_token = [&](Step st) -> int {
+        const int qp = min(st.qt * QBK + st.sb * QS + (lane & 31), N - 1);
+        return p.perm ? gload(p.perm + qp) : qp;
+    };
+    auto aux_fetch = [&](Step st, int tok, float* lr, float* dl, u32x4* mw) {
+        *lr = gload(p.lse + (int64_t)bh * N + tok);
+        *dl = gload(p.delta + (int64_t)bh * N + tok);
+        (*mw)[0] = gload(mask_src(st.mask0, st.sb) + lane);
+        (*mw)[1] = gload(mask_src(st.mask1, st.sb) + lane);
         if constexpr (BIAS) {
-            (*mw)[2] = part_word(st.mask0, st.sb);
-            (*mw)[3] = part_word(st.mask1, st.sb);
+            (*mw)[2] = gload(part_src(st.mask0, st.sb) + lane);
+            (*mw)[3] = gload(part_src(st.mask1, st.sb) + lane);
         }
     };
-    auto aux_store = [&](float lv, float dl, u32x4 mw, float* aux) {
+    auto aux_store = [&](Step st, float lr, float dl, u32x4 mw, float* aux) {
         const int t = lane & 31;
         const int a = t >> 4, rem = t & 15;
         const int pos = 16 * (rem & 1) + 8 * a + 4 * ((rem >> 1) & 1) + (rem >> 2);
+        const bool valid = aux_valid(st);
         if (lane < 32) {
-            aux[pos] = lv;
-            aux[QS + pos] = dl;
+            aux[pos] = lse_log2(BIAS ? lr - p.lse_shift : lr, valid);
+            aux[QS + pos] = valid ? dl : 0.f;
         }
-        ((uint32_t*)aux)[2 * QS + lane] = mw[0];
-        ((uint32_t*)aux)[4 * QS + lane] = mw[1];
+        // a tile attended without a mask keeps every bit
+        ((uint32_t*)aux)[2 * QS + lane] = st.mask0 == -1 ? ~0u : mw[0];
+        ((uint32_t*)aux)[4 * QS + lane] = st.mask1 == -1 ? ~0u : mw[1];
         if constexpr (BIAS) {
             ((uint32_t*)aux)[6 * QS + lane] = mw[2];
             ((uint32_t*)aux)[8 * QS + lane] = mw[3];
@@ -584,25 +591,32 @@ void attn_bwd_dkdv(NaBwdParams p) {
         int tok[BPW];
         tokens(cur, tok);
         issue(tok, rows0);
-        float lv, dl;
+        float lr, dl;
         u32x4 mw = {0u, 0u, 0u, 0u};
+        int atok = 0;   // wave 0: the query token of step nx for lse / delta
         if (wave == 0) {
-            aux_fetch(cur, &lv, &dl, &mw);
-            aux_store(lv, dl, mw, aux0);
+            aux_fetch(cur, aux_token(cur), &lr, &dl, &mw);
+            aux_store(cur, lr, dl, mw, aux0);
         }
         int tok_n[BPW];
-        if (nx.e < t1) tokens(nx, tok_n);
+        if (nx.e < t1) {
+            tokens(nx, tok_n);
+            if (wave == 0) atok = aux_token(nx);
+        }
         auto step = [&](const uint16_t* rl, const float* al, uint16_t* rn, float* an) {
             wait_vmem();
             __syncthreads();
             const Step nn = nx.e < t1 ? next_step(nx) : nx;
             if (nx.e < t1) {
                 issue(tok_n, rn);
-                if (wave == 0) aux_fetch(nx, &lv, &dl, &mw);
-                if (nn.e < t1) tokens(nn, tok_n);
+                if (wave == 0) aux_fetch(nx, atok, &lr, &dl, &mw);
+                if (nn.e < t1) {
+                    tokens(nn, tok_n);
+                    if (wave == 0) atok = aux_token(nn);
+                }
             }
             compute(cur, rl, al);
-            if (nx.e < t1 && wave == 0) aux_store(lv, dl, mw, an);
+            if (nx.e < t1 && wave == 0) aux_store(nx, lr, dl, mw, an);
             cur = nx;
             nx = nn;
         };
