@@ -132,9 +132,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the (batch, head) slices shard with no communication; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. The "
+              "(batch, head) slices are independent, so N GPUs would each run this kernel on "
+              "1/N of them with no communication. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
