@@ -365,13 +365,108 @@ void attn_fwd_bf16(NaAttnParams p) {
     if (!qvalid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = (uint16_t*)p.out + b * p.o_sb + h * p.o_sh + (int64_t)qtok * p.o_sn;
+    // pi-Attention's separate softmax ("pi-Attention", Section 3.5, Eq. 15):
+    // the softmax over this query's online partners x - pi (and x + pi; Eq. 9),
+    // a separate distribution whose weighted value average is added to the
+    // window's.  Each half-wave holds half of q (elements 16 s + 8 half ..
+    // +7), so the partial dot products of the two halves are summed across
+    // lanes l and l ^ 32; an absent partner reads a clamped row and gets
+    // weight 0, so both halves always take part.
+    // At D = 64 every load (key and value rows of both partners) is issued
+    // first, so the tail pays one memory round trip; at D = 128 that many
+    // registers would spill, and the value rows are read at the store.
+    constexpr bool PRELOAD = D == 64;
+    float pw[2] = {0.f, 0.f};
+    const uint16_t* prow[2] = {vbase, vbase};
+    uint2 pv[2][DB][4];   // PRELOAD: this lane's 4-element groups of the partners' value rows
+    if constexpr (!BIAS) {
+        if (p.sep_skip > 0) {   // uniform
+            bool has[2];
+            float z[2];
+            // q . k over this lane's half of the head dimension (the explicit
+            // (uint32_t) matters: hipcc miscompiles a bit_cast of a bare
+            // vector element, giving every j word 0)
+            auto half_dot = [&](const u32x4* kw) {
+                float dot = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) {
+                    const u32x4 qw = __builtin_bit_cast(u32x4, qf[s2]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)qw[j]),
+                                                              __builtin_bit_cast(bf16x2, (uint32_t)kw[s2][j]),
+                                                              dot, false);
+                }
+                return dot;
+            };
+            // partner t's row (sequence position x -/+ pi, clamped) and whether it exists
+            auto partner = [&](int t, const uint16_t** krow) {
+                const int x = t == 0 ? qpos - p.sep_skip : qpos + p.sep_skip;
+                has[t] = t == 0 ? x >= 0 : (p.sep_both != 0 && x < N);
+                const int xc = min(max(x, 0), N - 1);
+                const int tok = p.perm ? p.perm[xc] : xc;
+                *krow = kbase + (int64_t)tok * p.k_sn + 8 * half;
+                prow[t] = vbase + (int64_t)tok * p.v_sn;
+            };
+            if constexpr (PRELOAD) {
+                u32x4 kw[2][KS];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const uint16_t* krow;
+                    partner(t, &krow);
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) kw[t][s2] = *(const u32x4*)(krow + 16 * s2);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            pv[t][db][g] = *(const uint2*)(prow[t] + 32 * db + 8 * g + 4 * half);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) z[t] = has[t] ? halves_sum(half_dot(kw[t])) * c : kNegInf;
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const uint16_t* krow;
+                    partner(t, &krow);
+                    u32x4 kw[KS];
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) kw[s2] = *(const u32x4*)(krow + 16 * s2);
+                    z[t] = has[t] ? halves_sum(half_dot(kw)) * c : kNegInf;   // log2 domain
+                }
+            }
+            const float m = fmaxf(z[0], z[1]);
+            if (m > kNegInf) {
+                const float e0 = has[0] ? fast_exp2(z[0] - m) : 0.f;
+                const float e1 = has[1] ? fast_exp2(z[1] - m) : 0.f;
+                const float il = 1.f / (e0 + e1);
+                pw[0] = e0 * il;
+                pw[1] = e1 * il;
+            }
+        }
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = 32 * db + 8 * g + 4 * half;
-            const f32x2 x0 = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv};
-            const f32x2 x1 = {o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = o[db][4 * g + i] * inv;
+            if constexpr (!BIAS) {
+                if (p.sep_skip > 0) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const uint2 vw = PRELOAD ? pv[t][db][g] : *(const uint2*)(prow[t] + d);
+                        y[0] = __builtin_fmaf(pw[t], __builtin_bit_cast(float, vw.x << 16), y[0]);
+                        y[1] = __builtin_fmaf(pw[t], __builtin_bit_cast(float, vw.x & 0xffff0000u), y[1]);
+                        y[2] = __builtin_fmaf(pw[t], __builtin_bit_cast(float, vw.y << 16), y[2]);
+                        y[3] = __builtin_fmaf(pw[t], __builtin_bit_cast(float, vw.y & 0xffff0000u), y[3]);
+                    }
+                }
+            }
+            const f32x2 x0 = {y[0], y[1]};
+            const f32x2 x1 = {y[2], y[3]};
             const uint2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(x0, bf16x2)),
                              __builtin_bit_cast(uint32_t, __builtin_convertvector(x1, bf16x2))};
             *(uint2*)(orow + d) = w;

@@ -322,6 +322,13 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         a.lse_shift = (float)std::log(alpha);
     }
     const int64_t N = p->n_tokens, D = d.head_dim, eb = elem_bytes(p);
+    // the bf16 kernels with 32 queries per wave take the separate softmax's
+    // partner branch in their epilogue; the others run it as a second kernel
+    const bool sep_fused = separate && d.dtype == NA_BF16 && d.q_block != 192;
+    if (sep_fused) {
+        a.sep_skip = d.skip;
+        a.sep_both = d.skip_both;
+    }
 
     if (n_wg == 0) return NA_OK;
     int rc = 0;
@@ -370,7 +377,7 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
             rc = na_permute_launch(ls, lse, B, H, N, 4, H * N * 4, N * 4, 4, H * N * 4, N * 4, 4,
                                    p->d_perm, 1, stream);
     }
-    if (rc == 0 && separate) {
+    if (rc == 0 && separate && !sep_fused) {
         // the partner branch of the separate-softmax variant, added to out
         NaSkipParams sp{};
         sp.q = q->ptr, sp.k = k->ptr, sp.v = v->ptr, sp.out = out->ptr;

@@ -118,6 +118,11 @@ struct NaAttnParams {
     const uint32_t* skip_masks;
     float skip_bias;
     float lse_shift;
+    // separate-softmax partner branch fused into the epilogue of the bf16
+    // kernels with 32 queries per wave (0 = none): the partner distance on the
+    // sequence and whether x + pi is fetched too
+    int32_t sep_skip;
+    int32_t sep_both;
 };
 
 // Gradient launch parameters (attn_bwd.hip).  Tensors as in NaAttnParams;

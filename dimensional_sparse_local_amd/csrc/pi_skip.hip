@@ -6,6 +6,10 @@
 // fetched; Eq. 9), and the weighted average of their values is added to the
 // output (Eq. 11 with the weights of Eq. 15).
 //
+// This kernel serves the fp32 kernels and the 48-query bf16 kernel (q_block
+// 192); the bf16 kernels with 32 queries per wave take the same branch in
+// their epilogue.
+//
 // One group of G lanes per query row, 16 bytes of each row per lane: the group
 // reduces its partial dot products by shuffles, takes the (at most 2-way)
 // softmax and accumulates the partners' value rows into the output row, which

@@ -204,8 +204,9 @@ size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t
  * kv_block): bf16 with head_dim 64 or 128 and (q_block, kv_block) =
  * (128, 64), (192, 64) or (256, 64), (64, 64) at head_dim 64 and (384, 64) at head_dim 128;
  * fp32 with head_dim 32 or 64 and (32, 32).  Fixed fusion (NA_SKIP_FIXED_FUSION) runs in bf16 only, at q_block 128
- * or 256 (or 64 at head_dim 64).  The separate-softmax mode enqueues a second kernel
- * after the attention kernel: it adds each query's partner softmax to out.
+ * or 256 (or 64 at head_dim 64).  The separate-softmax mode adds each query's
+ * partner softmax to out: in the attention kernel's epilogue for bf16 at every
+ * q_block except 192, otherwise in a second kernel enqueued after it.
  * In bf16 the probabilities are rounded to bf16 before they enter both P.V and
  * the row sum, so lse carries a relative row-sum error of at most 2^-8. */
 na_status na_forward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,

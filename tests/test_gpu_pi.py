@@ -7,8 +7,10 @@ Tolerances as for every other pattern (fp32 1e-5; bf16 max-abs 2e-2, relative
 L2 5e-3, lse 4e-3), since the partner only adds keys (and, for fixed fusion,
 one fp32 addition to their logits).  The separate variant's output is the
 window's weighted average plus a whole partner value row, so it is no longer
-bounded by max |v|; its window part is rounded to bf16 and the sum rounded
-again, each at most 2^-9 relative.  Its bound is therefore elementwise:
+bounded by max |v|; where the partner branch runs as its own kernel (fp32,
+and bf16 at q_block 192) the window part is rounded to bf16 and the sum
+rounded again, each at most 2^-9 relative (the other bf16 kernels add the
+branch before their one rounding).  Its bound is therefore elementwise:
 |error| <= 2e-2 + 2^-8 |reference| (bf16), with the same relative L2 bound.
 """
 import os
