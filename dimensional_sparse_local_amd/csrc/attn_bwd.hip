@@ -380,10 +380,13 @@ void attn_bwd_dkdv(NaBwdParams p) {
     const bool kvalid = kpos < N;
     const int ktok = kvalid ? (p.perm ? p.perm[kpos] : kpos) : 0;
     bf16x8 kf[KS];
-    // The V fragments wait in LDS (each lane reads back its own 16-byte words,
-    // one read per dP MFMA): 32 registers fewer, which lets two waves share a
-    // SIMD and hide each other's LDS and softmax latency.
-    __shared__ __attribute__((aligned(16))) u32x4 vfrag[NW * KS * 64];
+    // At D = 128 the V fragments wait in LDS (each lane reads back its own
+    // 16-byte words, one read per dP MFMA): 32 registers fewer, which lets two
+    // waves share a SIMD and hide each other's LDS and softmax latency.  At
+    // D = 64 they fit in registers (16) at the same occupancy.
+    constexpr bool VREG = D == 64;
+    __shared__ __attribute__((aligned(16))) u32x4 vfrag[VREG ? 1 : NW * KS * 64];
+    u32x4 vreg[KS];
     {
         const uint16_t* krow = (const uint16_t*)p.k + b * p.k_sb + h * p.k_sh + (int64_t)ktok * p.k_sn;
         const uint16_t* vrow = (const uint16_t*)p.v + b * p.v_sb + h * p.v_sh + (int64_t)ktok * p.v_sn;
@@ -395,7 +398,8 @@ void attn_bwd_dkdv(NaBwdParams p) {
                 x = *(const u32x4*)(vrow + 16 * s + 8 * half);
             }
             kf[s] = __builtin_bit_cast(bf16x8, w);
-            vfrag[(wave * KS + s) * 64 + lane] = x;
+            if constexpr (VREG) vreg[s] = x;
+            else vfrag[(wave * KS + s) * 64 + lane] = x;
         }
     }
     const uint16_t* qbase = (const uint16_t*)p.q + b * p.q_sb + h * p.q_sh;
@@ -529,7 +533,7 @@ void attn_bwd_dkdv(NaBwdParams p) {
             for (int ks = 0; ks < KS; ++ks) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qr + 16 * ks), kf[ks], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(gr + 16 * ks),
-                                                             __builtin_bit_cast(bf16x8, vfrag[(wave * KS + ks) * 64 + lane]), dp, 0,
+                                                             __builtin_bit_cast(bf16x8, VREG ? vreg[ks] : vfrag[(wave * KS + ks) * 64 + lane]), dp, 0,
                                                              0, 0);
             }
         }
