@@ -97,13 +97,17 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
     return __builtin_bit_cast(bf16x8, w);
 }
 
-// acc + sum of the 8 bf16 values of v (exact products with 1, fp32 sums).
-__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+// Sum of the 32 values of two 16-element accumulators, as a pairwise tree
+// (fp32 adds, depth 5).
+__device__ __forceinline__ float tile_sum32(const f32x16& a, const f32x16& b) {
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = a[r] + b[r];
+#pragma unroll
+    for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+        for (int r = 0; r < w; ++r) t[r] = t[r] + t[r + w];
+    return t[0];
 }
 
 // Combine a value across the two half-waves (lanes l and l ^ 32).  The swap

@@ -294,6 +294,9 @@ void attn_fwd_bf16(NaAttnParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+        // the row sum takes the fp32 probabilities, before their rounding to
+        // bf16 for P V, so lse carries fp32 rounding only
+        l_run += tile_sum32(s[0], s[1]);
         mfma_phase(std::true_type{});
         // O^T += V^T P^T, 16 keys per step.  Step ks covers accumulator
         // elements r0 = 8*(ks%2) .. r0+7 of score block ks/2: slot e of half h
@@ -305,8 +308,6 @@ void attn_fwd_bf16(NaAttnParams p) {
             const int r0 = 8 * (ks % 2);
             const bf16x8 bp = cvt8(sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
                                    sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]);
-            // the row sum takes the same bf16-rounded P that enters P V
-            l_run = sum_bf16x8(bp, l_run);
             const uint16_t* vr = vl + tr_base + 16 * ks * ROW;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -504,12 +505,11 @@ __device__ __forceinline__ float quad_sum(float x) {
     return halves_sum(__builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]));
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_m16(NaAttnParams p) {
-    constexpr int NW = 4;
     constexpr int QBN = 3;                       // 16-query blocks per wave
-    constexpr int QB = 16 * QBN * NW;            // 192
+    constexpr int QB = 16 * QBN * NW;            // 192 or 384
     constexpr int KV = NA_KV_BLOCK_BF16;
     constexpr int ROW = D + 8;
     constexpr int CS = D / 8 + 1;
@@ -695,7 +695,9 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
             for (int qb = 0; qb < QBN; ++qb) {
                 bp[qb] = cvt8(s[0][qb][0], s[0][qb][1], s[0][qb][2], s[0][qb][3], s[1][qb][0],
                               s[1][qb][1], s[1][qb][2], s[1][qb][3]);
-                l_run[qb] = sum_bf16x8(bp[qb], l_run[qb]);
+                // fp32 row sum of the probabilities before their bf16 rounding
+                l_run[qb] += ((s[0][qb][0] + s[0][qb][1]) + (s[0][qb][2] + s[0][qb][3])) +
+                             ((s[1][qb][0] + s[1][qb][1]) + (s[1][qb][2] + s[1][qb][3]));
             }
             // O^T += V^T P^T: the transpose reads give slot j' of group g the
             // row 32*hs + 4*j' + cg (first read) or + 16 (second read)
@@ -937,9 +939,9 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
         else if (head_dim == 64 && q_block == 256)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 8>), grid, dim3(512), 0, st, p);
         else if (head_dim == 128 && q_block == 192)
-            hipLaunchKernelGGL((attn_fwd_bf16_m16<128>), grid, dim3(256), 0, st, p);
+            hipLaunchKernelGGL((attn_fwd_bf16_m16<128, 4>), grid, dim3(256), 0, st, p);
         else if (head_dim == 64 && q_block == 192)
-            hipLaunchKernelGGL((attn_fwd_bf16_m16<64>), grid, dim3(256), 0, st, p);
+            hipLaunchKernelGGL((attn_fwd_bf16_m16<64, 4>), grid, dim3(256), 0, st, p);
         else
             return (int)hipErrorInvalidValue;
     } else {

@@ -207,8 +207,8 @@ size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t
  * or 256 (or 64 at head_dim 64).  The separate-softmax mode adds each query's
  * partner softmax to out: in the attention kernel's epilogue for bf16 at every
  * q_block except 192, otherwise in a second kernel enqueued after it.
- * In bf16 the probabilities are rounded to bf16 before they enter both P.V and
- * the row sum, so lse carries a relative row-sum error of at most 2^-8. */
+ * In bf16 the probabilities are rounded to bf16 for the P.V product only; the
+ * row sum (and so lse) adds them in fp32. */
 na_status na_forward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
                      const na_tensor* k, const na_tensor* v, const na_tensor* out, float* lse,
                      float scale, uint32_t flags, void* workspace, size_t workspace_bytes,
