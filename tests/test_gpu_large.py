@@ -20,7 +20,7 @@ from dimensional_sparse_local_amd import workloads as W
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": dict(abs=1e-5, lse=1e-5), "bf16": dict(abs=2e-2, lse=4e-3)}
+TOL = {"fp32": dict(abs=1e-5, lse=1e-5), "bf16": dict(abs=2e-2, lse=1e-3)}
 REL_L2 = 1e-2
 MAX_REL = 2e-2
 

@@ -1,12 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
 Tolerances: fp32 max-abs 1e-5; bf16 max-abs 2e-2 and relative L2 5e-3 on the
-output.  LSE: 1e-5 (fp32) and 4e-3 (bf16).  In bf16 the kernel rounds every
-probability to bf16 (round to nearest even, relative error at most 2^-8) before
-it enters both the P.V product and the row sum, so the output stays a properly
-normalised average of v while the row sum may differ from the exact one by a
-factor in [1 - 2^-8, 1 + 2^-8]: |lse error| <= -ln(1 - 2^-8) ~= 3.92e-3, plus a
-few fp32 ulps of |scale * q.k|.
+output.  LSE: 1e-5 (fp32) and 1e-3 (bf16).  In bf16 the kernel rounds every
+probability to bf16 (round to nearest even) for the P.V product only; the row
+sum adds the fp32 probabilities, so lse carries fp32 rounding of the logits,
+the exponentials, the sum and the log: a few ulps of |scale * q.k|, far inside
+1e-3.
 Small cases compare every element; the full-size workloads compare sampled
 query rows (all grid corners plus seeded random rows), launched exactly as the
 benchmark launches them.
@@ -23,7 +22,7 @@ from dimensional_sparse_local_amd import workloads as W
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=4e-3)}
+TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=1e-3)}
 
 
 def _na():

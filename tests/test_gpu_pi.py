@@ -4,7 +4,7 @@ oracle on the same bits: the union working set with one softmax (Eq. 11),
 fixed fusion's log-prior logits (Eqs. 16-17) and the separate softmax of
 Eq. 15, causal and bidirectional, on 1-D sequences and on the Hilbert curve.
 Tolerances as for every other pattern (fp32 1e-5; bf16 max-abs 2e-2, relative
-L2 5e-3, lse 4e-3), since the partner only adds keys (and, for fixed fusion,
+L2 5e-3, lse 1e-3), since the partner only adds keys (and, for fixed fusion,
 one fp32 addition to their logits).  The separate variant's output is the
 window's weighted average plus a whole partner value row, so it is no longer
 bounded by max |v|; where the partner branch runs as its own kernel (fp32,
@@ -24,7 +24,7 @@ from dimensional_sparse_local_amd import workloads as W
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=4e-3)}
+TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=1e-3)}
 
 
 def _na():
@@ -132,7 +132,7 @@ def test_pi_full_size(name):
     o = out[:1].float().cpu().numpy().astype(np.float64)
     _check_out(wl, o, ref_out)
     assert np.linalg.norm(o - ref_out) / np.linalg.norm(ref_out) <= 5e-3
-    assert np.max(np.abs(lse[:1].cpu().numpy() - ref_lse)) <= 4e-3
+    assert np.max(np.abs(lse[:1].cpu().numpy() - ref_lse)) <= 1e-3
 
 
 GRAD_CASES = [

@@ -9,7 +9,7 @@ in its union, fixed-fusion and separate-softmax forms), an order (row-major,
 tiled with random tiles, Hilbert), a dtype and head_dim the kernels support
 and one of the query tiles available for it. Every output element and every
 lse is compared with the oracle at the parity tolerances (bf16: max-abs 2e-2,
-relative L2 5e-3, lse 4e-3, with 2^-8 of the reference added elementwise for
+relative L2 5e-3, lse 1e-3, with 2^-8 of the reference added elementwise for
 the separate softmax, whose output is not bounded by max |v|; fp32: 1e-5).
 Every third bf16 case whose query tile the gradients support also compares dq,
 dk and dv (relative L2 1e-2, max-abs 2e-2 of the largest reference magnitude).
@@ -26,7 +26,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 N_CASES = 160
-TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=4e-3)}
+TOL = {"fp32": dict(abs=1e-5, rel=None, lse=1e-5), "bf16": dict(abs=2e-2, rel=5e-3, lse=1e-3)}
 Q_BLOCKS = {("bf16", 64): [64, 128, 192, 256], ("bf16", 128): [128, 192, 256, 384],
             ("fp32", 32): [0], ("fp32", 64): [0]}
 
