@@ -64,11 +64,15 @@ __device__ __forceinline__ float keep_if(uint32_t w, int bit, float x) {
     return (w >> bit) & 1u ? x : kNegInf;
 }
 
-// Online softmax in the log2 domain with a lazy rescale: a row's reference
-// maximum moves (and O, l are rescaled) only when the tile maximum exceeds it
-// by more than 2^8, which keeps every P <= 256 and is exact after the final
-// division by l.
-constexpr float kRescaleLog2 = 8.0f;
+// Online softmax in the log2 domain against a reference maximum per row: the
+// probabilities of a tile are 2^(c s - reference); the reference moves (and O,
+// l are rescaled) only when a row has none yet or when one lane's sum of a
+// tile's probabilities, which bounds each of them, passes 2^kSumLog2.  Every
+// probability then stays below 2^32, far inside fp32 and bf16 range for O and
+// l over any number of keys, and the result is exact after the final division
+// by l whatever the reference.
+constexpr float kSumLog2 = 32.0f;
+constexpr float kSumMax = 4294967296.0f;   // 2^kSumLog2
 
 typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;

@@ -56,9 +56,10 @@ __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : (D == 64 && NW >= 4 && !BIAS ? 4 : 2),
                                    NW > 8 ? 3 : (D == 64 && NW >= 4 && !BIAS ? 4 : 2))))
 void attn_fwd_bf16(NaAttnParams p) {
-    using MaskT = typename MaskRow<BIAS>::T;
     constexpr int KV = NA_KV_BLOCK_BF16;
     constexpr int QB = 32 * NW;
+    constexpr int MP = BIAS ? 2 : 1;             // mask planes: keep (and fixed fusion's partners)
+    constexpr int MB = (QB * 8 + 1023) / 1024;   // 1 KB DMA blocks per mask plane
     constexpr int ROW = D + 8;                   // padded LDS row (elements)
     constexpr int CS = D / 8 + 1;                // 16-byte slots per padded row
     constexpr int TILE = KV * ROW;               // LDS elements per tensor tile
@@ -71,6 +72,10 @@ void attn_fwd_bf16(NaAttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
+    // mask rows of the tile (two 32-key words per query row and plane), DMA'd
+    // with K and V when the tile carries a mask
+    __shared__ __attribute__((aligned(1024))) u32x2 m_lds0[MP][QB];
+    __shared__ __attribute__((aligned(1024))) u32x2 m_lds1[MP][QB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -106,71 +111,44 @@ void attn_fwd_bf16(NaAttnParams p) {
 
     // DMA block j = wave + NW*i moves slots 64*j .. 64*j+63 of a tile; lane t
     // moves slot 64*j + t = (row, chunk) with CS slots per row; chunk CS-1 is
-    // the pad and comes from the zero page.
-    int dma_row[IPW], dma_ch[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int slot = 64 * (wave + NW * i) + lane;
-        dma_row[i] = slot / CS;
-        dma_ch[i] = slot % CS;
-    }
-    // Pad slots copy chunk 0 of their row (never read back), so every slot of a
-    // tile that ends before the last token has a real source address.
-    int dma_off[IPW];   // element offset of this lane's chunk inside its row
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) dma_off[i] = dma_ch[i] < CS - 1 ? 8 * dma_ch[i] : 0;
+    // the row's pad and re-reads chunk 0 (never read back), so every slot has a
+    // real source.  Recomputed where used (CS is a compile-time constant).
+    auto dma_row = [&](int i) { return (64 * (wave + NW * i) + lane) / CS; };
+    auto dma_cb = [&](int i) {
+        const uint32_t ch = (64 * (wave + NW * i) + lane) % CS;
+        return ch < CS - 1 ? 16u * ch : 0u;
+    };
     // Token of the row this lane moves in each of its DMA blocks, fetched one
-    // step ahead (clamped to a valid token).  Its value is not used before the
-    // DMA is issued, so fetching it never waits.
+    // step ahead.  Rows past the last token (the ragged last tile) are clamped
+    // to the last token: the tile's mask excludes those keys, so their scores
+    // are -inf and their probabilities exactly 0.  Its value is not used
+    // before the DMA is issued, so fetching it never waits.
     auto tokens = [&](NaEntry entry, int* tok) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int kp = min(entry.kt * KV + dma_row[i], N - 1);
+            const int kp = min(entry.kt * KV + dma_row(i), N - 1);
             tok[i] = p.perm ? gload(p.perm + kp) : kp;
         }
     };
-    auto issue = [&](NaEntry entry, const int* tok, uint16_t* kl, uint16_t* vl) {
-        // offsets inside one (batch, head) slice fit in 32 bits (checked on the host)
-        if (entry.kt * KV + KV <= N) {
+    // Sources as a uniform base plus a 32-bit byte offset (a (batch, head)
+    // slice spans fewer than 2^31 elements, checked on the host).
+    const char* kb8 = (const char*)kbase;
+    const char* vb8 = (const char*)vbase;
+    const uint32_t k_rb = 2u * (uint32_t)p.k_sn, v_rb = 2u * (uint32_t)p.v_sn;
+    auto issue = [&](NaEntry entry, const int* tok, uint16_t* kl, uint16_t* vl, u32x2 (*ml)[QB]) {
+        if (entry.mask >= 0 && wave < MB * MP) {   // mask rows: 128 per block, two per lane
+            const int plane = wave / MB, row = 128 * (wave % MB) + 2 * lane;
+            const uint32_t* src = plane == 0 ? p.masks : p.skip_masks;
+            if (row < QB) dma16(src + ((int64_t)entry.mask * QB + row) * 2, &ml[plane][row - 2 * lane]);
+        }
 #pragma unroll
-            for (int i = 0; i < IPW; ++i) {
-                const int blk = wave + NW * i;
-                if (blk < NI) {  // wave-uniform
-                    dma16(kbase + ((uint32_t)tok[i] * (uint32_t)p.k_sn + dma_off[i]), kl + blk * 512);
-                    dma16(vbase + ((uint32_t)tok[i] * (uint32_t)p.v_sn + dma_off[i]), vl + blk * 512);
-                }
-            }
-        } else {
-            // the last tile: rows past the last token come from the zero page
-#pragma unroll
-            for (int i = 0; i < IPW; ++i) {
-                const int blk = wave + NW * i;
-                if (blk < NI) {
-                    const bool real = entry.kt * KV + dma_row[i] < N;
-                    const uint16_t* gk = real ? kbase + ((uint32_t)tok[i] * (uint32_t)p.k_sn + dma_off[i])
-                                              : (const uint16_t*)p.zero;
-                    const uint16_t* gv = real ? vbase + ((uint32_t)tok[i] * (uint32_t)p.v_sn + dma_off[i])
-                                              : (const uint16_t*)p.zero;
-                    dma16(gk, kl + blk * 512);
-                    dma16(gv, vl + blk * 512);
-                }
+        for (int i = 0; i < IPW; ++i) {
+            const int blk = wave + NW * i;
+            if (blk < NI) {  // wave-uniform
+                dma16(kb8 + ((uint32_t)tok[i] * k_rb + dma_cb(i)), kl + blk * 512);
+                dma16(vb8 + ((uint32_t)tok[i] * v_rb + dma_cb(i)), vl + blk * 512);
             }
         }
-    };
-    auto mask_row = [&](NaEntry entry) {
-        MaskT w = {};
-        if (entry.mask >= 0) {
-            const int64_t at = ((int64_t)entry.mask * QB + mrow) * 2;
-            const u32x2 keep = gload((const u32x2*)(p.masks + at));
-            w[0] = keep[0];
-            w[1] = keep[1];
-            if constexpr (BIAS) {
-                const u32x2 part = gload((const u32x2*)(p.skip_masks + at));
-                w[2] = part[0];
-                w[3] = part[1];
-            }
-        }
-        return w;
     };
 
     f32x16 o[DB];
@@ -204,13 +182,13 @@ void attn_fwd_bf16(NaAttnParams p) {
             else __builtin_amdgcn_s_setprio(0);
         }
     };
-    auto compute = [&](NaEntry entry, MaskT mk, const uint16_t* kl, const uint16_t* vl) {
+    // S^T = K Q^T for the two 32-key halves of the tile, masked where the tile
+    // is partial (or runs past the last key).
+    auto scores = [&](NaEntry entry, const u32x2 (*ml)[QB], const uint16_t* kl, f32x16* s) {
         mfma_phase(std::true_type{});
-        // S^T = K Q^T for the two 32-key halves of the tile.  All KS fragments
-        // of the first half are requested up front; each MFMA of the first
-        // half is then followed by the request for the matching fragment of
-        // the second half, so LDS latency hides behind MFMA work.
-        f32x16 s[2];
+        // All KS fragments of the first half are requested up front; each MFMA
+        // of the first half is then followed by the request for the matching
+        // fragment of the second half, so LDS latency hides behind MFMA work.
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.f;
         if constexpr (NW > 8) {
@@ -251,6 +229,7 @@ void attn_fwd_bf16(NaAttnParams p) {
         // element mask (partial tiles and tiles past the last key only): score
         // (kb, r) is key 32*kb + 16*(r/8) + 2*(r/4 % 2) + half + 4*(r % 4)
         if (entry.mask >= 0) {
+            const u32x2 mk = ml[0][mrow];
             const uint32_t w0 = mk[0] >> half, w1 = mk[1] >> half;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -261,7 +240,8 @@ void attn_fwd_bf16(NaAttnParams p) {
             if constexpr (BIAS) {
                 // fixed fusion: partners outside the window carry the extra
                 // log-prior, as an offset of the raw dot product
-                const uint32_t b0 = mk[2] >> half, b1 = mk[3] >> half;
+                const u32x2 bk = ml[1][mrow];
+                const uint32_t b0 = bk[0] >> half, b1 = bk[1] >> half;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int bit = 16 * (r / 8) + 2 * ((r / 4) % 2) + 4 * (r % 4);
@@ -270,33 +250,52 @@ void attn_fwd_bf16(NaAttnParams p) {
                 }
             }
         }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-        mx = halves_max(mx);
-        const float m_tile = mx * c;
-        const bool grow = m_tile > m_ref + kRescaleLog2;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-            // rows that do not grow keep alpha = 1 (their m_ref may still be -inf)
-            const float m_new = grow ? m_tile : m_ref;
-            const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
-            m_ref = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        }
+    };
+    // s <- 2^(c s - m_ref), fp32; returns this lane's sum of them.  A row with
+    // no reference yet (m_ref = -inf) takes 0 here and is redone below.
+    auto probs = [&](f32x16* s) {
         const float neg_m = m_ref == kNegInf ? 0.f : -m_ref;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+        return tile_sum32(s[0], s[1]);
+    };
+    auto compute = [&](NaEntry entry, const u32x2 (*ml)[QB], const uint16_t* kl, const uint16_t* vl) {
+        f32x16 s[2];
+        scores(entry, ml, kl, s);
+        // Online softmax against a reference maximum that moves only when it
+        // must: the probabilities are taken against the row's current
+        // reference, and the exact tile maximum is formed only if a row has no
+        // reference yet or a lane's sum of this tile's probabilities (which
+        // bounds each of them) passes 2^kSumLog2.  Then the wave recomputes the
+        // scores and moves every row's reference to max(reference, tile
+        // maximum), rescaling O and l; the result is exact after the final
+        // division by l either way.
+        float ts = probs(s);
+        const bool redo = m_ref == kNegInf || !(ts <= kSumMax);
+        if (__builtin_amdgcn_ballot_w64(redo)) {
+            scores(entry, ml, kl, s);
+            float mx = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+            const float m_new = fmaxf(m_ref, halves_max(mx) * c);   // both halves of a row agree
+            if (m_new > m_ref) {
+                const float alpha = fast_exp2(m_ref - m_new);   // 0 when m_ref = -inf
+                m_ref = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            }
+            ts = probs(s);
+        }
         // the row sum takes the fp32 probabilities, before their rounding to
         // bf16 for P V, so lse carries fp32 rounding only
-        l_run += tile_sum32(s[0], s[1]);
+        l_run += ts;
         mfma_phase(std::true_type{});
         // O^T += V^T P^T, 16 keys per step.  Step ks covers accumulator
         // elements r0 = 8*(ks%2) .. r0+7 of score block ks/2: slot e of half h
@@ -321,44 +320,37 @@ void attn_fwd_bf16(NaAttnParams p) {
     };
 
     // ---- pipelined walk over the CSR row ------------------------------------
-    // Entering step e: tile e is in flight to (or in) its LDS buffer, ent_a..c
-    // are the entries of tiles e..e+2, tok_n the tokens of tile e+1 and mk_a /
-    // mk_b the mask rows of tiles e / e+1.
+    // Entering step e: tile e (K, V and its mask rows) is in flight to (or in)
+    // its LDS buffers, ent_a..c are the entries of tiles e..e+2 and tok_n the
+    // tokens of tile e+1.
     const int e0 = cload(p.row_ptr + qt), e1 = cload(p.row_ptr + qt + 1);
     const NaEntry none = {0, -1};
     NaEntry ent_a = none, ent_b = none, ent_c = none;
     int tok_n[IPW];
-    MaskT mk_a = {}, mk_b = {};
     if (e0 < e1) {
         ent_a = load_entry(p.entries + e0);
         if (e0 + 1 < e1) ent_b = load_entry(p.entries + e0 + 1);
         if (e0 + 2 < e1) ent_c = load_entry(p.entries + e0 + 2);
         int tok0[IPW];
         tokens(ent_a, tok0);
-        issue(ent_a, tok0, k_lds0, v_lds0);
-        mk_a = mask_row(ent_a);
-        if (e0 + 1 < e1) {
-            tokens(ent_b, tok_n);
-            mk_b = mask_row(ent_b);
-        }
+        issue(ent_a, tok0, k_lds0, v_lds0, m_lds0);
+        if (e0 + 1 < e1) tokens(ent_b, tok_n);
     }
-    auto step = [&](int e, const uint16_t* kl, const uint16_t* vl, uint16_t* kn, uint16_t* vn) {
+    auto step = [&](int e, const uint16_t* kl, const uint16_t* vl, const u32x2 (*ml)[QB], uint16_t* kn,
+                    uint16_t* vn, u32x2 (*mn)[QB]) {
         wait_vmem();
         __syncthreads();
-        if (e + 1 < e1) issue(ent_b, tok_n, kn, vn);
+        if (e + 1 < e1) issue(ent_b, tok_n, kn, vn, mn);
         if (e + 2 < e1) tokens(ent_c, tok_n);
-        const MaskT mk_c = e + 2 < e1 ? mask_row(ent_c) : MaskT{};
         const NaEntry ent_d = e + 3 < e1 ? load_entry(p.entries + e + 3) : none;
-        compute(ent_a, mk_a, kl, vl);
+        compute(ent_a, ml, kl, vl);
         ent_a = ent_b;
         ent_b = ent_c;
         ent_c = ent_d;
-        mk_a = mk_b;
-        mk_b = mk_c;
     };
     for (int e = e0; e < e1; e += 2) {
-        step(e, k_lds0, v_lds0, k_lds1, v_lds1);
-        if (e + 1 < e1) step(e + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+        step(e, k_lds0, v_lds0, m_lds0, k_lds1, v_lds1, m_lds1);
+        if (e + 1 < e1) step(e + 1, k_lds1, v_lds1, m_lds1, k_lds0, v_lds0, m_lds0);
     }
 
     // ---- epilogue -----------------------------------------------------------
@@ -560,12 +552,13 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     const uint16_t* vbase = (const uint16_t*)p.v + b * p.v_sb + h * p.v_sh;
 
     // ---- DMA of one key/value tile (as in the 32-query kernel) -----------------
-    // slot -> (row, element offset of the chunk); recomputed where used to save
-    // registers (CS is a compile-time constant)
+    // slot -> (row, byte offset of the chunk); recomputed where used to save
+    // registers (CS is a compile-time constant).  Rows past the last token are
+    // clamped to it (masked keys, probability exactly 0).
     auto dma_row = [&](int i) { return (64 * (wave + NW * i) + lane) / CS; };
-    auto dma_off = [&](int i) {
-        const int ch = (64 * (wave + NW * i) + lane) % CS;
-        return ch < CS - 1 ? 8 * ch : 0;
+    auto dma_cb = [&](int i) {
+        const uint32_t ch = (64 * (wave + NW * i) + lane) % CS;
+        return ch < CS - 1 ? 16u * ch : 0u;
     };
     auto tokens = [&](NaEntry entry, int* tok) {
 #pragma unroll
@@ -574,35 +567,22 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
             tok[i] = p.perm ? gload(p.perm + kp) : kp;
         }
     };
+    const char* kb8 = (const char*)kbase;
+    const char* vb8 = (const char*)vbase;
+    const uint32_t k_rb = 2u * (uint32_t)p.k_sn, v_rb = 2u * (uint32_t)p.v_sn;
     auto issue = [&](NaEntry entry, const int* tok, uint16_t* kl, uint16_t* vl, u32x2* ml) {
-        // the tile's mask rows: QB rows of 8 bytes = 1.5 KB, two DMA blocks
+        // the tile's mask rows: QB rows of 8 bytes, 1 KB (128 rows) per wave
         if (entry.mask >= 0 && wave < (QB * 8) / 1024 + 1) {
             const int row = 128 * wave + lane * 2;   // two 8-byte rows per lane
             if (row < QB)
                 dma16(p.masks + ((int64_t)entry.mask * QB + row) * 2, ml + 128 * wave);
         }
-        if (entry.kt * KV + KV <= N) {
 #pragma unroll
-            for (int i = 0; i < IPW; ++i) {
-                const int blk = wave + NW * i;
-                if (blk < NI) {
-                    dma16(kbase + ((uint32_t)tok[i] * (uint32_t)p.k_sn + dma_off(i)), kl + blk * 512);
-                    dma16(vbase + ((uint32_t)tok[i] * (uint32_t)p.v_sn + dma_off(i)), vl + blk * 512);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < IPW; ++i) {
-                const int blk = wave + NW * i;
-                if (blk < NI) {
-                    const bool real = entry.kt * KV + dma_row(i) < N;
-                    const uint16_t* gk = real ? kbase + ((uint32_t)tok[i] * (uint32_t)p.k_sn + dma_off(i))
-                                              : (const uint16_t*)p.zero;
-                    const uint16_t* gv = real ? vbase + ((uint32_t)tok[i] * (uint32_t)p.v_sn + dma_off(i))
-                                              : (const uint16_t*)p.zero;
-                    dma16(gk, kl + blk * 512);
-                    dma16(gv, vl + blk * 512);
-                }
+        for (int i = 0; i < IPW; ++i) {
+            const int blk = wave + NW * i;
+            if (blk < NI) {
+                dma16(kb8 + ((uint32_t)tok[i] * k_rb + dma_cb(i)), kl + blk * 512);
+                dma16(vb8 + ((uint32_t)tok[i] * v_rb + dma_cb(i)), vl + blk * 512);
             }
         }
     };
@@ -622,82 +602,103 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     const int pi = 4 * (pim & 3) + 2 * ((pim >> 2) & 1) + (pim >> 3);
     const int tr_base = (4 * (q16 >> 2) + cg) * ROW + 4 * (q16 & 3);
 
-    auto compute = [&](NaEntry entry, const u32x2* ml, const uint16_t* kl, const uint16_t* vl) {
+    // S^T blocks of one 32-key half: keys 32*hs + 16*kb .. +15, queries of
+    // block qb; masked where the tile is partial (or runs past the last key).
+    auto scores = [&](int hs, NaEntry entry, const u32x2* ml, const uint16_t* kl, f32x4 (*s)[QBN]) {
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {   // two 32-key halves of the tile
-            // S^T blocks: keys 32*hs + 16*kb .. +15, queries of block qb
-            f32x4 s[2][QBN];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int qb = 0; qb < QBN; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            // k-step outer, one step of lookahead: fragments of both 16-key
+            // blocks for step ks+1 load while the 6 MFMAs of step ks run
+            const uint16_t* kr = kl + (32 * hs + pi) * ROW + 8 * g;
+            bf16x8 a0 = *(const bf16x8*)(kr);
+            bf16x8 a1 = *(const bf16x8*)(kr + 16 * ROW);
 #pragma unroll
-                for (int qb = 0; qb < QBN; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            {
-                // k-step outer, one step of lookahead: fragments of both 16-key
-                // blocks for step ks+1 load while the 6 MFMAs of step ks run
-                const uint16_t* kr = kl + (32 * hs + pi) * ROW + 8 * g;
-                bf16x8 a0 = *(const bf16x8*)(kr);
-                bf16x8 a1 = *(const bf16x8*)(kr + 16 * ROW);
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    bf16x8 n0 = a0, n1 = a1;
-                    if (ks + 1 < KS) {
-                        n0 = *(const bf16x8*)(kr + 32 * (ks + 1));
-                        n1 = *(const bf16x8*)(kr + 16 * ROW + 32 * (ks + 1));
-                    }
-#pragma unroll
-                    for (int qb = 0; qb < QBN; ++qb) {
-                        s[0][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[qb][ks], s[0][qb], 0, 0, 0);
-                        s[1][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[qb][ks], s[1][qb], 0, 0, 0);
-                    }
-                    a0 = n0;
-                    a1 = n1;
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 n0 = a0, n1 = a1;
+                if (ks + 1 < KS) {
+                    n0 = *(const bf16x8*)(kr + 32 * (ks + 1));
+                    n1 = *(const bf16x8*)(kr + 16 * ROW + 32 * (ks + 1));
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // element mask: element i of block kb is key 32*hs + 16*kb + 4*i + cg
-            if (entry.mask >= 0) {
 #pragma unroll
                 for (int qb = 0; qb < QBN; ++qb) {
-                    const uint32_t w = ml[wave * (16 * QBN) + 16 * qb + q16][hs] >> cg;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) s[kb][qb][i] = keep_if(w, 16 * kb + 4 * i, s[kb][qb][i]);
+                    s[0][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[qb][ks], s[0][qb], 0, 0, 0);
+                    s[1][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[qb][ks], s[1][qb], 0, 0, 0);
                 }
+                a0 = n0;
+                a1 = n1;
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // element mask: element i of block kb is key 32*hs + 16*kb + 4*i + cg
+        if (entry.mask >= 0) {
 #pragma unroll
             for (int qb = 0; qb < QBN; ++qb) {
-                float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3]));
-                mx = fmaxf(mx, fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
-                mx = quad_max(mx);
-                const float m_tile = mx * c;
-                const bool grow = m_tile > m_ref[qb] + kRescaleLog2;
-                if (__builtin_amdgcn_ballot_w64(grow)) {
-                    const float m_new = grow ? m_tile : m_ref[qb];
-                    const float alpha = grow ? fast_exp2(m_ref[qb] - m_new) : 1.f;
-                    m_ref[qb] = m_new;
-                    l_run[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) o[db][qb][i] *= alpha;
-                }
-                const float neg_m = m_ref[qb] == kNegInf ? 0.f : -m_ref[qb];
+                const uint32_t w = ml[wave * (16 * QBN) + 16 * qb + q16][hs] >> cg;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        s[kb][qb][i] = fast_exp2(__builtin_fmaf(s[kb][qb][i], c, neg_m));
+                    for (int i = 0; i < 4; ++i) s[kb][qb][i] = keep_if(w, 16 * kb + 4 * i, s[kb][qb][i]);
             }
+        }
+    };
+    // s <- 2^(c s - m_ref) per query block, fp32; ts[qb] = this lane's sums.
+    auto probs = [&](f32x4 (*s)[QBN], float* ts) {
+#pragma unroll
+        for (int qb = 0; qb < QBN; ++qb) {
+            const float neg_m = m_ref[qb] == kNegInf ? 0.f : -m_ref[qb];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[kb][qb][i] = fast_exp2(__builtin_fmaf(s[kb][qb][i], c, neg_m));
+            ts[qb] = ((s[0][qb][0] + s[0][qb][1]) + (s[0][qb][2] + s[0][qb][3])) +
+                     ((s[1][qb][0] + s[1][qb][1]) + (s[1][qb][2] + s[1][qb][3]));
+        }
+    };
+
+    auto compute = [&](NaEntry entry, const u32x2* ml, const uint16_t* kl, const uint16_t* vl) {
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {   // two 32-key halves of the tile
+            f32x4 s[2][QBN];
+            scores(hs, entry, ml, kl, s);
+            // online softmax against each row's reference maximum, which moves
+            // only for a row with none yet or a lane sum past 2^kSumLog2 (the
+            // wave then recomputes the half's scores and takes exact maxima)
+            float ts[QBN];
+            probs(s, ts);
+            bool redo = false;
+#pragma unroll
+            for (int qb = 0; qb < QBN; ++qb) redo = redo || m_ref[qb] == kNegInf || !(ts[qb] <= kSumMax);
+            if (__builtin_amdgcn_ballot_w64(redo)) {
+                scores(hs, entry, ml, kl, s);
+#pragma unroll
+                for (int qb = 0; qb < QBN; ++qb) {
+                    float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3]));
+                    mx = fmaxf(mx, fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
+                    const float m_new = fmaxf(m_ref[qb], quad_max(mx) * c);   // the row's four lanes agree
+                    if (m_new > m_ref[qb]) {
+                        const float alpha = fast_exp2(m_ref[qb] - m_new);   // 0 when m_ref = -inf
+                        m_ref[qb] = m_new;
+                        l_run[qb] *= alpha;
+#pragma unroll
+                        for (int db = 0; db < DB; ++db)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) o[db][qb][i] *= alpha;
+                    }
+                }
+                probs(s, ts);
+            }
+            // fp32 row sums of the probabilities before their bf16 rounding
+#pragma unroll
+            for (int qb = 0; qb < QBN; ++qb) l_run[qb] += ts[qb];
             // P^T operands: slot j = 4*kb + i of lane-group g is key 32*hs + 16*kb + 4*i + cg
             bf16x8 bp[QBN];
 #pragma unroll
             for (int qb = 0; qb < QBN; ++qb) {
                 bp[qb] = cvt8(s[0][qb][0], s[0][qb][1], s[0][qb][2], s[0][qb][3], s[1][qb][0],
                               s[1][qb][1], s[1][qb][2], s[1][qb][3]);
-                // fp32 row sum of the probabilities before their bf16 rounding
-                l_run[qb] += ((s[0][qb][0] + s[0][qb][1]) + (s[0][qb][2] + s[0][qb][3])) +
-                             ((s[1][qb][0] + s[1][qb][1]) + (s[1][qb][2] + s[1][qb][3]));
             }
             // O^T += V^T P^T: the transpose reads give slot j' of group g the
             // row 32*hs + 4*j' + cg (first read) or + 16 (second read)
