@@ -105,6 +105,17 @@ def lib():
     return _lib
 
 
+def _same_bh(B: int, H: int, **tensors):
+    """Raise ValueError unless every given tensor (None skipped) is 4-D with
+    leading dimensions (B, H)."""
+    for name, x in tensors.items():
+        if x is None:
+            continue
+        if x.dim() != 4 or (int(x.shape[0]), int(x.shape[1])) != (B, H):
+            raise ValueError("%s has shape %s; it must be [B, H, N, D] with B=%d, H=%d"
+                             % (name, tuple(x.shape), B, H))
+
+
 def _check(status: int):
     if status != NA_OK:
         raise NaError(status, lib().na_last_error().decode())
@@ -267,9 +278,9 @@ class Plan:
         import torch
 
         B, H = int(q.shape[0]), int(q.shape[1])
-        for x in (k, v):
-            if tuple(x.shape[:2]) != (B, H):
-                raise ValueError("q, k, v must share B and H")
+        # every tensor the kernels write or read must cover (B, H): the C ABI
+        # takes pointers and strides only, so a smaller one would be overrun
+        _same_bh(B, H, k=k, v=v, out=out)
         if out is None:
             out = torch.empty_like(q, memory_format=torch.contiguous_format)
         if lse is True:
@@ -285,6 +296,8 @@ class Plan:
         ws_bytes = int(lib().na_forward_workspace_bytes(self._h, B, H, flags))
         if ws_bytes and workspace is None:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        if ws_bytes:   # the library checks the size the caller actually supplied
+            ws_bytes = workspace.numel() * workspace.element_size()
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
         ts = [self._tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
@@ -304,9 +317,11 @@ class Plan:
         import torch
 
         B, H = int(q.shape[0]), int(q.shape[1])
-        for x in (k, v, out, dout):
-            if tuple(x.shape[:2]) != (B, H):
-                raise ValueError("q, k, v, out, dout must share B and H")
+        _same_bh(B, H, k=k, v=v, out=out, dout=dout)
+        if grads is not None:
+            if len(grads) != 3:
+                raise ValueError("grads must be (dq, dk, dv)")
+            _same_bh(B, H, dq=grads[0], dk=grads[1], dv=grads[2])
         if (lse.dtype != torch.float32 or not lse.is_contiguous()
                 or tuple(lse.shape) != (B, H, self.n_tokens)):
             raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
@@ -319,6 +334,7 @@ class Plan:
         ws_bytes = int(lib().na_backward_workspace_bytes(self._h, B, H))
         if workspace is None:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
         ts = [self._tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"),
@@ -334,6 +350,7 @@ class Plan:
         """Rows gathered into the plan's order (or scattered back with inverse)."""
         import torch
 
+        _same_bh(int(x.shape[0]), int(x.shape[1]), out=out)
         if out is None:
             out = torch.empty_like(x, memory_format=torch.contiguous_format)
         if stream is None:

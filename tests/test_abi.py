@@ -72,3 +72,60 @@ def test_workspace_size():
     assert na.lib().na_forward_workspace_bytes(p._h, 2, 3, 0) == 0
     ws = na.lib().na_forward_workspace_bytes(p._h, 2, 3, na.NA_FWD_PERMUTE_PASSES)
     assert ws >= 4 * 2 * 3 * 1024 * 64 * 2 + 2 * 3 * 1024 * 4
+
+
+# ---------------------------------------------------------------------------
+# The binding checks every tensor's (B, H) before any device call: the C ABI
+# sees pointers and strides only, so a tensor with fewer batches or heads than
+# q would be written past its end.  These run on the CPU (host-only plan, CPU
+# tensors): the shape check comes first and raises ValueError.
+# ---------------------------------------------------------------------------
+
+def _bh_case():
+    torch = pytest.importorskip("torch")
+    wl = dict(grid=[64], pattern=dict(kind="band", left=2, right=2), D=64, dtype="bf16")
+    plan = na.Plan(wl, host_only=True)
+    mk = lambda B, H: torch.zeros((B, H, 64, 64), dtype=torch.bfloat16)
+    return torch, plan, mk
+
+
+def test_forward_rejects_out_with_fewer_heads():
+    torch, plan, mk = _bh_case()
+    q = mk(2, 3)
+    with pytest.raises(ValueError, match="out"):
+        plan.forward(q, mk(2, 3), mk(2, 3), out=mk(2, 2))
+    with pytest.raises(ValueError, match="out"):
+        plan.forward(q, mk(2, 3), mk(2, 3), out=mk(1, 3))
+
+
+def test_forward_rejects_k_v_mismatch():
+    torch, plan, mk = _bh_case()
+    with pytest.raises(ValueError, match="k"):
+        plan.forward(mk(2, 3), mk(2, 1), mk(2, 3))
+    with pytest.raises(ValueError, match="v"):
+        plan.forward(mk(2, 3), mk(2, 3), mk(1, 3))
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_backward_rejects_small_grads(which):
+    torch, plan, mk = _bh_case()
+    x = mk(2, 3)
+    lse = torch.zeros((2, 3, 64), dtype=torch.float32)
+    grads = [mk(2, 3), mk(2, 3), mk(2, 3)]
+    grads[which] = mk(2, 1)
+    with pytest.raises(ValueError, match=("dq", "dk", "dv")[which]):
+        plan.backward(x, x, x, x, lse, x, grads=tuple(grads))
+
+
+def test_backward_rejects_dout_mismatch():
+    torch, plan, mk = _bh_case()
+    x = mk(2, 3)
+    lse = torch.zeros((2, 3, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="dout"):
+        plan.backward(x, x, x, x, lse, mk(2, 2))
+
+
+def test_permute_rejects_small_out():
+    torch, plan, mk = _bh_case()
+    with pytest.raises(ValueError, match="out"):
+        plan.permute(mk(2, 3), out=mk(2, 2))

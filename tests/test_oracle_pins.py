@@ -94,6 +94,31 @@ def test_hilbert_defining_properties(n):
         k *= 2
 
 
+# The classic Hilbert curve written out by hand ("Hilbert-Guided Sparse Local
+# Attention", Methodology in Plain English: tokens are reordered along a
+# Hilbert curve; the orientation is the reading that the curve starts at row 0,
+# column 0 and ends at row 0, column n - 1, x = column, y = row).  On 4 x 4 the
+# curve visits the 2 x 2 quadrants rows 0-1 / cols 0-1, rows 2-3 / cols 0-1,
+# rows 2-3 / cols 2-3, rows 0-1 / cols 2-3 (a U), walking the first one along
+# row 0 first and leaving the last one at row 0: perm[p] = row * 4 + col.
+HILBERT_4X4 = [0, 1, 5, 4, 8, 12, 13, 9, 10, 14, 15, 11, 7, 6, 2, 3]
+
+
+def test_hilbert_literal_4x4():
+    assert oracle.hilbert(4).tolist() == HILBERT_4X4
+    # the generalised curve reduces to the same literal order on this square
+    assert oracle.hilbert_grid(4, 4).tolist() == HILBERT_4X4
+
+
+def test_hilbert_literal_128_ends():
+    # 128 x 128: the curve opens with (0,0), (1,0), (1,1), (0,1) (row, col):
+    # a 2 x 2 block walked down, right, up, since an odd number of levels
+    # (7) transposes the first block; it closes at row 0, column 127.
+    perm = oracle.hilbert(128)
+    assert perm[:4].tolist() == [0, 128, 129, 1]
+    assert int(perm[-1]) == 127
+
+
 def test_hilbert_invalid_side():
     with pytest.raises(ValueError):
         oracle.hilbert(96)

@@ -93,6 +93,16 @@ def test_hilbert_order_matches_oracle(n):
     assert np.array_equal(p.order().astype(np.int64), oracle.hilbert(n))
 
 
+def test_hilbert_order_literals():
+    # the planner's curve against the hand-written classic order (4 x 4) and
+    # the 128 x 128 curve's ends, the same literals the oracle is pinned to
+    four = _plan(dict(grid=[4, 4], order="hilbert", pattern=dict(kind="band", left=1, right=1)), 16, 16)
+    assert four.order().tolist() == [0, 1, 5, 4, 8, 12, 13, 9, 10, 14, 15, 11, 7, 6, 2, 3]
+    big = _plan(dict(grid=[128, 128], order="hilbert", pattern=dict(kind="band", left=1, right=1)), 16, 16)
+    perm = big.order()
+    assert perm[:4].tolist() == [0, 128, 129, 1] and int(perm[-1]) == 127
+
+
 def _random_workload(rng):
     kind = rng.choice(["na", "sa", "band", "blocked", "sta", "hilbert"])
     if kind == "band":
