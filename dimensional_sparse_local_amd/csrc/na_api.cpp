@@ -6,7 +6,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
+#include <limits>
 #include <new>
 
 #include "na_internal.h"
@@ -195,6 +197,29 @@ na_status na_plan_get_stats(na_plan_t p, na_plan_stats* s) {
         return NA_ERR_INVALID_ARG;
     }
     *s = p->stats;
+    return NA_OK;
+}
+
+na_status na_plan_get_bounds(na_plan_t p, na_plan_bounds* out) {
+    if (!p || !out) {
+        na_set_error("plan or bounds pointer is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    const int64_t N = p->stats.n_tokens, qb = p->stats.q_block, kb = p->stats.kv_block;
+    const int64_t nq = p->stats.n_q_tiles, nk = p->stats.n_kv_tiles;
+    const int64_t visited = p->stats.n_partial + p->stats.n_full;
+    const int64_t pairs = p->stats.attended_pairs;
+    // token pairs inside the visited tiles, ragged last tiles at their true size
+    int64_t inside = 0;
+    for (int64_t qt = 0; qt < nq; ++qt) {
+        const int64_t qs = std::min(qb, N - qt * qb);
+        for (int32_t e = p->row_ptr[qt]; e < p->row_ptr[qt + 1]; ++e)
+            inside += qs * std::min(kb, N - (int64_t)p->entries[e].kt * kb);
+    }
+    const double inf = std::numeric_limits<double>::infinity();
+    out->flop = pairs > 0 ? (double)N * (double)N / (double)pairs : inf;
+    out->tile = visited > 0 ? (double)nq * (double)nk / (double)visited : inf;
+    out->useful_fraction = inside > 0 ? (double)pairs / (double)inside : 1.0;
     return NA_OK;
 }
 

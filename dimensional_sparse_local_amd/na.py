@@ -48,6 +48,11 @@ class Stats(ctypes.Structure):
         "n_full", "attended_pairs")]
 
 
+class Bounds(ctypes.Structure):
+    _fields_ = [("flop", ctypes.c_double), ("tile", ctypes.c_double),
+                ("useful_fraction", ctypes.c_double)]
+
+
 class Tensor(ctypes.Structure):
     _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
                 ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
@@ -64,7 +69,7 @@ _STATUS = {NA_ERR_INVALID_ARG: "invalid argument", NA_ERR_UNSUPPORTED: "unsuppor
            NA_ERR_PLAN_MISMATCH: "plan mismatch"}
 
 _lib = None
-ABI_VERSION = 3  # NA_ABI_VERSION of include/na.h that Desc mirrors
+ABI_VERSION = 4  # NA_ABI_VERSION of include/na.h that Desc mirrors
 
 
 def lib():
@@ -79,6 +84,7 @@ def lib():
         L.na_plan_create.argtypes = [P(Desc), u32, P(vp)]
         L.na_plan_destroy.argtypes = [vp]
         L.na_plan_get_stats.argtypes = [vp, P(Stats)]
+        L.na_plan_get_bounds.argtypes = [vp, P(Bounds)]
         L.na_plan_get_classes.argtypes = [vp, vp, ctypes.c_size_t]
         L.na_plan_get_order.argtypes = [vp, vp, ctypes.c_size_t]
         L.na_forward_workspace_bytes.argtypes = [vp, i64, i64, u32]
@@ -95,7 +101,8 @@ def lib():
         L.na_status_string.restype = ctypes.c_char_p
         L.na_last_error.restype = ctypes.c_char_p
         L.na_abi_version.restype = ctypes.c_int32
-        for f in ("na_plan_create", "na_plan_destroy", "na_plan_get_stats", "na_plan_get_classes",
+        for f in ("na_plan_create", "na_plan_destroy", "na_plan_get_stats", "na_plan_get_bounds",
+                  "na_plan_get_classes",
                   "na_plan_get_order", "na_forward", "na_permute", "na_backward"):
             getattr(L, f).restype = ctypes.c_int
         if L.na_abi_version() != ABI_VERSION:
@@ -245,18 +252,9 @@ class Plan:
         * ``useful_fraction``: attended pairs / pairs inside non-empty tiles
           (1.0 when every visited tile is full: a perfectly block-sparse map).
         """
-        st = self.stats
-        n = st["n_tokens"]
-        visited = st["n_partial"] + st["n_full"]
-        pairs = st["attended_pairs"]
-        # pairs inside the visited tiles, with the ragged last tiles at their true size
-        q_sizes = np.minimum(st["q_block"], n - np.arange(st["n_q_tiles"]) * st["q_block"])
-        k_sizes = np.minimum(st["kv_block"], n - np.arange(st["n_kv_tiles"]) * st["kv_block"])
-        visited_rows = self.classes() != 0
-        inside = int(np.sum(q_sizes * (visited_rows @ k_sizes.astype(np.int64))))
-        return {"flop": n * n / pairs if pairs else float("inf"),
-                "tile": st["n_q_tiles"] * st["n_kv_tiles"] / visited if visited else float("inf"),
-                "useful_fraction": pairs / inside if inside else 1.0}
+        b = Bounds()
+        _check(lib().na_plan_get_bounds(self._h, ctypes.byref(b)))
+        return {"flop": b.flop, "tile": b.tile, "useful_fraction": b.useful_fraction}
 
     # -- device calls --------------------------------------------------------
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define NA_ABI_VERSION 3
+#define NA_ABI_VERSION 4
 
 typedef enum {
     NA_OK = 0,
@@ -162,6 +162,16 @@ typedef struct {
                                            |window| + |partners| for NA_SKIP_SEPARATE */
 } na_plan_stats;
 
+/* Speedup bounds of a pattern over dense attention of the same length and
+ * tiles, from the tile map alone. */
+typedef struct {
+    double flop;            /* N^2 / attended pairs: what counting flops promises */
+    double tile;            /* (n_q_tiles * n_kv_tiles) / non-empty tile pairs: what a kernel that
+                               skips empty tiles and pays in full for every other one can reach */
+    double useful_fraction; /* attended pairs / token pairs inside the non-empty tiles (ragged
+                               last tiles at their true size); 1 for a perfectly block-sparse map */
+} na_plan_bounds;
+
 typedef struct {
     void* ptr;                          /* device pointer to element [0, 0, 0, 0] */
     int64_t stride_b, stride_h, stride_n; /* in elements; the D axis has stride 1 */
@@ -175,21 +185,42 @@ typedef struct na_plan_s* na_plan_t;
  * tile in CSR form, and (unless NA_PLAN_HOST_ONLY) upload order, CSR and the
  * per-token mask tables to the current device.  The plan owns all of it and is
  * immutable afterwards; it may be used from several streams at once.
+ * Defined by: the block classes empty / partial / full and the reordering
+ * path computed once and cached ("Hilbert-Guided Sparse Local Attention",
+ * Methodology in Plain English); tiles sharing one window with the tile equal
+ * to the kernel block ("ENA: Efficient N-dimensional Attention", core claim).
+ * desc and plan are caller-owned host memory; *plan receives a handle the
+ * caller releases with na_plan_destroy.
  * Returns NA_ERR_INVALID_ARG for a malformed descriptor, NA_ERR_UNSUPPORTED for
- * a Hilbert order on a grid that is not 2-D. */
+ * a Hilbert order on a grid that is not 2-D, NA_ERR_OUT_OF_MEMORY or
+ * NA_ERR_DEVICE if a host or device allocation or upload fails (nothing is
+ * leaked). */
 na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* plan);
 
 /* Release a plan (host and device memory).  The caller must first make sure
  * that no enqueued work still uses it.  NULL is accepted. */
 na_status na_plan_destroy(na_plan_t plan);
 
+/* Tile-map statistics into caller-owned host memory (same source as
+ * na_plan_create); attended_pairs sets the effective flops 4 * D * pairs * B * H. */
 na_status na_plan_get_stats(na_plan_t plan, na_plan_stats* stats);
 
-/* Dense class matrix uint8 [n_q_tiles][n_kv_tiles]: 0 empty, 1 partial, 2 full.
- * n must be at least n_q_tiles * n_kv_tiles. */
+/* Speedup bounds of the plan's tile map (the realistic-bound simulator that
+ * "Generalized Neighborhood Attention", Abstract, describes), into
+ * caller-owned host memory.  NA_ERR_INVALID_ARG on NULL arguments. */
+na_status na_plan_get_bounds(na_plan_t plan, na_plan_bounds* bounds);
+
+/* Dense class matrix uint8 [n_q_tiles][n_kv_tiles]: 0 empty, 1 partial, 2 full
+ * ("Hilbert-Guided Sparse Local Attention", Methodology in Plain English: a
+ * block is empty, full, or partial and needs element masks), into
+ * caller-owned host memory; n must be at least n_q_tiles * n_kv_tiles
+ * (NA_ERR_INVALID_ARG otherwise). */
 na_status na_plan_get_classes(na_plan_t plan, uint8_t* host_classes, size_t n);
 
-/* perm[p] = row-major token at sequence position p; n must be >= N. */
+/* perm[p] = row-major token at sequence position p (the order tokens are
+ * reordered into, e.g. along the Hilbert curve: "Hilbert-Guided Sparse Local
+ * Attention", Abstract), into caller-owned host memory; n must be >= N
+ * (NA_ERR_INVALID_ARG otherwise). */
 na_status na_plan_get_order(na_plan_t plan, int32_t* host_perm, size_t n);
 
 /* Workspace bytes na_forward needs for (B, H) with the given flags (0 for the
@@ -197,7 +228,13 @@ na_status na_plan_get_order(na_plan_t plan, int32_t* host_perm, size_t n);
 size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t flags);
 
 /* out = softmax attention of q over its neighbourhood keys/values, lse as
- * above.  q, k, v, out share the plan's dtype and head_dim; lse may be NULL;
+ * above: out_i = sum_j exp(z_ij - lse_i) v_j over the neighbourhood of i, with
+ * z_ij = scale q_i . k_j ("pi-Attention", Section 3.1, Eqs. 1-3, restricted
+ * to the neighbourhood as in Section 3.2, Eqs. 4-5).  q, k, v, out are
+ * caller-owned device tensors and lse a caller-owned device buffer; nothing is
+ * allocated (the permute-passes path uses the caller's workspace, >=
+ * na_forward_workspace_bytes, 256-byte aligned).  q, k, v, out share the
+ * plan's dtype and head_dim; lse may be NULL;
  * scale must be finite and positive (NA_ERR_INVALID_ARG otherwise).
  * Returns NA_ERR_PLAN_MISMATCH if the plan was built host-only, and
  * NA_ERR_UNSUPPORTED if no kernel matches (dtype, head_dim, q_block,
@@ -248,12 +285,21 @@ na_status na_backward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
 
 /* Row gather along the plan's order: out[b, h, p, :] = in[b, h, perm[p], :]
  * (inverse = 0) or out[b, h, perm[p], :] = in[b, h, p, :] (inverse = 1), for
- * the plan's dtype and head_dim.  in and out must not overlap. */
+ * the plan's dtype and head_dim: the reordering of tokens along the curve and
+ * back ("Hilbert-Guided Sparse Local Attention", Abstract and Methodology in
+ * Plain English).  in and out are caller-owned device tensors and must not
+ * overlap.  NA_ERR_UNSUPPORTED for a plan whose order is the identity,
+ * NA_ERR_PLAN_MISMATCH for a host-only plan or another device, NA_ERR_DEVICE if
+ * the launch fails.  Asynchronous on stream. */
 na_status na_permute(na_plan_t plan, int64_t B, int64_t H, const na_tensor* in,
                      const na_tensor* out, int32_t inverse, void* stream);
 
+/* Static name of a status code ("unknown status" for other values). */
 const char* na_status_string(na_status status);
+/* Detail of the calling thread's last failure (valid until its next call). */
 const char* na_last_error(void);
+/* NA_ABI_VERSION the library was built with; a binding compares it with the
+ * header it mirrors. */
 int32_t na_abi_version(void);
 
 #ifdef __cplusplus

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = na.lib()
-    assert lib.na_abi_version() == na.ABI_VERSION == 3
+    assert lib.na_abi_version() == na.ABI_VERSION == 4
     for s in range(6):
         assert lib.na_status_string(s)
     assert lib.na_status_string(99) == b"unknown status"
@@ -49,6 +49,7 @@ def test_null_arguments():
     assert lib.na_backward(None, 1, 1, None, None, None, None, None, None, None, None, None, 1.0,
                            None, 0, None) == na.NA_ERR_INVALID_ARG
     assert lib.na_backward_workspace_bytes(None, 1, 1) == 0
+    assert lib.na_plan_get_bounds(None, None) == na.NA_ERR_INVALID_ARG
 
 
 def test_unknown_flags():

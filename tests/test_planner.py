@@ -279,6 +279,26 @@ def test_speedup_bounds():
     assert sb == {"flop": 1.0, "tile": 1.0, "useful_fraction": 1.0}
 
 
+def test_speedup_bounds_match_class_matrix():
+    # the C call against the same bounds counted here from the class matrix
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        n = int(rng.integers(1, 700))
+        wl = dict(grid=[n], pattern=dict(kind="band", left=int(rng.integers(0, 90)),
+                                         right=int(rng.integers(0, 90))), D=64, dtype="bf16")
+        qb = int(rng.choice([64, 128, 256]))
+        p = na.Plan(wl, host_only=True, q_block=qb)
+        st, cls = p.stats, p.classes()
+        qs = np.minimum(st["q_block"], n - np.arange(st["n_q_tiles"]) * st["q_block"])
+        ks = np.minimum(st["kv_block"], n - np.arange(st["n_kv_tiles"]) * st["kv_block"])
+        inside = int(np.sum(qs[:, None] * ks[None, :] * (cls != 0)))
+        visited = int(np.count_nonzero(cls))
+        got = p.speedup_bounds()
+        assert got["flop"] == pytest.approx(n * n / st["attended_pairs"])
+        assert got["tile"] == pytest.approx(cls.size / visited)
+        assert got["useful_fraction"] == pytest.approx(st["attended_pairs"] / inside)
+
+
 def test_pi_partner_tile_maps():
     """pi-Attention's partner (pi-Attention, Eqs. 8-9) in the tile map: union
     and fixed fusion put the partners into the map, the separate variant keeps
