@@ -49,6 +49,14 @@ def read_traffic(kernel_sig: str, workload: str, q_block: int):
     return None
 
 
+def _stats(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    med = ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+    return {"median": round(med, 4), "min": round(ys[0], 4), "max": round(ys[-1], 4),
+            "mean": round(sum(ys) / n, 4)}
+
+
 def kernel_signature() -> str:
     import hashlib
 
@@ -118,10 +126,13 @@ def main():
     ap.add_argument("--permute-passes", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
-                    help="time the forward (default) or the backward pass (dq, dk, dv from the "
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "permute"),
+                    default="forward",
+                    help="time the forward (default), the backward pass (dq, dk, dv from the "
                          "forward's out and lse; effective flops 10 * D per attended pair: the "
-                         "recomputed score and the dP, dV, dK, dQ products)")
+                         "recomputed score and the dP, dV, dK, dQ products), or the row gather "
+                         "along the plan's order alone (q into sequence order; GB/s of rows read "
+                         "and written against 8 TB/s)")
     ap.add_argument("--vs-dense", action="store_true",
                     help="also time dense attention of the same shape on the same kernel (window "
                          "= whole grid) and report the measured speedup beside the tile map's "
@@ -185,6 +196,15 @@ def main():
     def step():
         plan.forward(q, k, v, out=out, lse=lse, scale=scale, permute_passes=args.permute_passes)
 
+    if args.which == "permute":
+        if wl["order"] == "row_major" or internal:
+            raise SystemExit("--pass permute needs a workload with a tiled or Hilbert order")
+        gathered = torch.empty_like(q)
+        flops = 0
+
+        def step():
+            plan.permute(q, out=gathered)
+
     if args.which == "backward":
         if args.permute_passes:
             raise SystemExit("--permute-passes applies to the forward pass only")
@@ -204,22 +224,34 @@ def main():
     log("bench: warmup done")
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    # one HIP event after each step, on the stream the kernels run on: the
+    # per-step times (each step is one launch of the hot path)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
+        marks[i].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    log("bench: %.3f ms/step" % ms)
+    per_step = [start.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i])
+                                                  for i in range(1, args.steps)]
+    step_stats = _stats(per_step)
+    log("bench: %.3f ms/step (median %.3f, min %.3f, max %.3f)"
+        % (ms, step_stats["median"], step_stats["min"], step_stats["max"]))
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl["dtype"]]
     # Algorithmic HBM bytes per step: every tensor read or written once
     # (forward: q, k, v in, out and fp32 lse out; backward: q, k, v, out, dout
     # and lse in, dq, dk, dv out).
+    # Permute: each row read once and written once.
     n_rows = B * H * plan.n_tokens
-    row_tensors = 4 if args.which == "forward" else 8
-    alg_bytes = n_rows * (row_tensors * D * ELEM_BYTES[wl["dtype"]] + 4)
+    if args.which == "permute":
+        alg_bytes = n_rows * 2 * D * ELEM_BYTES[wl["dtype"]]
+    else:
+        row_tensors = 4 if args.which == "forward" else 8
+        alg_bytes = n_rows * (row_tensors * D * ELEM_BYTES[wl["dtype"]] + 4)
     hbm_bound = alg_bytes / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
 
@@ -261,8 +293,12 @@ def main():
         cpu = cpu_baseline(wl, q, k, v, scale, args.cpu_seconds)
 
     sig = kernel_signature()
+    value, unit = round(tflops, 3), "TFLOP/s"
     if name == W.HEADLINE and args.which == "forward":
         metric = METRIC
+    elif args.which == "permute":
+        metric = "row gather along the plan's order (GB/s read + written), %s" % wl.get("note", name)
+        value, unit = round(gbs, 1), "GB/s"
     else:
         metric = "effective TFLOP/s (unmasked FLOPs), %s%s" % (
             wl.get("note", name), ", backward pass" if args.which == "backward" else "")
@@ -273,15 +309,19 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4)}
-    roof.update({"traffic": traffic, "algorithmic_bytes": alg_bytes, "kernel_sig": sig})
+    roof.update({"traffic": traffic, "algorithmic_bytes": alg_bytes, "kernel_sig": sig,
+                 "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE on this kernel source, "
+                                    "committed in profiles/attn_fwd_sta3d_pmc.md"
+                                    if traffic is not None else None)})
     line = {
         "metric": metric,
-        "value": round(tflops, 3),
-        "unit": "TFLOP/s",
+        "value": value,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

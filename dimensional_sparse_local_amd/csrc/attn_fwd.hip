@@ -16,7 +16,6 @@
 // Local Attention", methodology).
 
 #include "attn_common.h"
-#include <type_traits>
 
 namespace {
 
@@ -26,19 +25,16 @@ namespace {
 // Two waves share every SIMD (<= 256 registers each), so the MFMA phase of one
 // overlaps the softmax phase of the other.  At D = 64 (128 registers) four
 // waves share a SIMD, so up to four workgroups per CU keep K/V requests in
-// flight for the short CSR rows of small windows.  With 12 waves (384 queries: one
-// 6x8x8 sliding tile) three waves share a SIMD (<= 168 registers): each K/V
-// tile staged from L2 then serves 1.5 times the queries, which is what limits
-// these kernels (staging the tiles, not the barriers or the waits, costs about
-// a third of the time at 256 queries).  K and V tiles travel from HBM/L2
-// straight into LDS (global_load_lds, 16 bytes per lane, no register staging)
-// into two statically selected buffers: while tile e is computed from one
-// buffer, tile e+1 streams into the other.  The gather addresses are prepared
-// ahead: the CSR entry of tile e+3 and the token indices of tile e+2 are
-// fetched while tile e is computed, so no dependent load stalls a step.
+// flight for the short CSR rows of small windows.  K and V tiles (and the mask
+// rows of a masked tile) travel from HBM/L2 straight into LDS (global_load_lds,
+// 16 bytes per lane, no register staging) into two statically selected
+// buffers: while tile e is computed from one buffer, tile e+1 streams into the
+// other.  The gather addresses are prepared ahead: the CSR entry of tile e+3
+// and the token indices of tile e+2 are fetched while tile e is computed, so
+// no dependent load stalls a step.
 //
 // LDS rows of K and V are padded by one 16-byte chunk (row stride D + 8
-// elements); the DMA fills the pad slots from a zero page, so one DMA block of
+// elements); the pad slot re-reads the row's first chunk, so one DMA block of
 // 64 lanes covers 64 consecutive (row, chunk) slots and K and V share one slot
 // -> row map.  Both operand reads are bank-conflict free at this stride: the K
 // operand reads one chunk from each of 16 consecutive rows per 16-lane phase,
@@ -46,15 +42,13 @@ namespace {
 // per half, +16 per step) of the tile, whose 32-byte segments fall on disjoint
 // banks; the P^T operand slots follow the same row order.
 //
-// Online softmax in the log2 domain with a lazy rescale: a row's reference
-// maximum moves (and O, l are rescaled) only when the tile maximum exceeds it
-// by more than 2^8, which keeps every P <= 256 and is exact after the final
-// division by l.
+// Online softmax in the log2 domain against a per-row reference maximum that
+// moves only when it must (see kSumLog2).
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool BIAS = false>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : (D == 64 && NW >= 4 && !BIAS ? 4 : 2),
-                                   NW > 8 ? 3 : (D == 64 && NW >= 4 && !BIAS ? 4 : 2))))
+__attribute__((amdgpu_waves_per_eu(D == 64 && NW >= 4 && !BIAS ? 4 : 2,
+                                   D == 64 && NW >= 4 && !BIAS ? 4 : 2)))
 void attn_fwd_bf16(NaAttnParams p) {
     constexpr int KV = NA_KV_BLOCK_BF16;
     constexpr int QB = 32 * NW;
@@ -173,37 +167,15 @@ void attn_fwd_bf16(NaAttnParams p) {
     // 32*db + 16*(g%2) + 4*(s%4).
     const int tr_base = (half + 4 * ((lane & 15) >> 2)) * ROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // With three waves per SIMD, a wave in an MFMA phase takes issue priority so
-    // that the others' softmax work fills the gaps instead of competing for the
-    // MFMA pipe (measured: 2 % on 384-query tiles; with two waves it costs 2 %).
-    auto mfma_phase = [&](auto on) {
-        if constexpr (NW > 8) {
-            if constexpr (decltype(on)::value) __builtin_amdgcn_s_setprio(1);
-            else __builtin_amdgcn_s_setprio(0);
-        }
-    };
     // S^T = K Q^T for the two 32-key halves of the tile, masked where the tile
     // is partial (or runs past the last key).
     auto scores = [&](NaEntry entry, const u32x2 (*ml)[QB], const uint16_t* kl, f32x16* s) {
-        mfma_phase(std::true_type{});
         // All KS fragments of the first half are requested up front; each MFMA
         // of the first half is then followed by the request for the matching
         // fragment of the second half, so LDS latency hides behind MFMA work.
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.f;
-        if constexpr (NW > 8) {
-            // three waves per SIMD (168 registers): one K fragment in flight,
-            // the compiler schedules the reads ahead as registers allow
-            const uint16_t* kr0 = kl + kappa * ROW + 8 * half;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 kf = *(const bf16x8*)(kr0 + 32 * ROW * kb + 16 * ks);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
-                }
-            }
-        } else {
+        {
             const uint16_t* kr0 = kl + kappa * ROW + 8 * half;
             const uint16_t* kr1 = kr0 + 32 * ROW;
             bf16x8 kf[KS];
@@ -225,7 +197,6 @@ void attn_fwd_bf16(NaAttnParams p) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);   // KS MFMAs
         }
-        mfma_phase(std::false_type{});
         // element mask (partial tiles and tiles past the last key only): score
         // (kb, r) is key 32*kb + 16*(r/8) + 2*(r/4 % 2) + half + 4*(r % 4)
         if (entry.mask >= 0) {
@@ -296,7 +267,6 @@ void attn_fwd_bf16(NaAttnParams p) {
         // the row sum takes the fp32 probabilities, before their rounding to
         // bf16 for P V, so lse carries fp32 rounding only
         l_run += ts;
-        mfma_phase(std::true_type{});
         // O^T += V^T P^T, 16 keys per step.  Step ks covers accumulator
         // elements r0 = 8*(ks%2) .. r0+7 of score block ks/2: slot e of half h
         // is key 16*ks + 2*(e/4) + h + 4*(e%4), the row the transpose reads
@@ -316,7 +286,6 @@ void attn_fwd_bf16(NaAttnParams p) {
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[db], 0, 0, 0);
             }
         }
-        mfma_phase(std::false_type{});
     };
 
     // ---- pipelined walk over the CSR row ------------------------------------
@@ -934,7 +903,7 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
         else if (head_dim == 128 && q_block == 256)
             hipLaunchKernelGGL((attn_fwd_bf16<128, 8>), grid, dim3(512), 0, st, p);
         else if (head_dim == 128 && q_block == 384)
-            hipLaunchKernelGGL((attn_fwd_bf16<128, 12>), grid, dim3(768), 0, st, p);
+            hipLaunchKernelGGL((attn_fwd_bf16_m16<128, 8>), grid, dim3(512), 0, st, p);
         else if (head_dim == 64 && q_block == 128)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 4>), grid, dim3(256), 0, st, p);
         else if (head_dim == 64 && q_block == 256)

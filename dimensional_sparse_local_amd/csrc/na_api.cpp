@@ -348,8 +348,9 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
     }
     const int64_t N = p->n_tokens, D = d.head_dim, eb = elem_bytes(p);
     // the bf16 kernels with 32 queries per wave take the separate softmax's
-    // partner branch in their epilogue; the others run it as a second kernel
-    const bool sep_fused = separate && d.dtype == NA_BF16 && d.q_block != 192;
+    // partner branch in their epilogue; the others (fp32, and the 48-query
+    // bf16 kernels at q_block 192 and 384) run it as a second kernel
+    const bool sep_fused = separate && d.dtype == NA_BF16 && d.q_block != 192 && d.q_block != 384;
     if (sep_fused) {
         a.sep_skip = d.skip;
         a.sep_both = d.skip_both;
