@@ -137,6 +137,10 @@ def main():
                     help="also time dense attention of the same shape on the same kernel (window "
                          "= whole grid) and report the measured speedup beside the tile map's "
                          "speedup bounds")
+    ap.add_argument("--plan-times", action="store_true",
+                    help="only time host plan creation (tile map, CSR, masks; no device upload) "
+                         "for the five named workloads at their benchmark query tiles: median of "
+                         "3, one JSON line each (runs without a GPU)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the row-permute kernel over 268,435,456 bytes (read once, "
                          "written once): the known-size copy that calibrates HBM counters")
@@ -147,6 +151,27 @@ def main():
               "(batch, head) slices are independent, so N GPUs would each run this kernel on "
               "1/N of them with no communication. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.plan_times:
+        from dimensional_sparse_local_amd import na
+        from dimensional_sparse_local_amd import workloads as W
+
+        for name, q_block in (("na2d_fp32", 0), ("na2d_bf16", 64), ("sta3d_bf16", 384),
+                              ("hilbert_band_bf16", 0), ("causal1d_bf16", 0)):
+            wl = W.CONFIGS[name]
+            if name == "na2d_bf16":   # the benchmark's internal 8x8 patch order
+                wl = W.scaled(wl, order="tiled", tile=[8, 8])
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                plan = na.Plan(wl, host_only=True, q_block=q_block)
+                ts.append(time.perf_counter() - t0)
+            st = plan.stats
+            print(json.dumps({"workload": name, "plan_ms": round(sorted(ts)[1] * 1e3, 2),
+                              "q_block": st["q_block"], "n_q_tiles": st["n_q_tiles"],
+                              "n_kv_tiles": st["n_kv_tiles"],
+                              "non_empty": st["n_partial"] + st["n_full"]}), flush=True)
+        return
 
     import torch
 

@@ -69,5 +69,35 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     return LIB
 
 
+def build_host_sanitized(path: str) -> str:
+    """libna.so at `path` with the host code (planner and C ABI) compiled by
+    g++ under AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+    device objects of the ordinary build (made first if missing).  For the CPU
+    sanitizer run of the planner tests; load it with the sanitizer runtime
+    preloaded."""
+    objdir = os.path.join(ROOT, "_build")
+    dev_objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in DEVICE_SOURCES]
+    if not all(os.path.exists(o) for o in dev_objs):
+        build()
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    san = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined"]
+    sdir = os.path.dirname(path)
+    os.makedirs(sdir, exist_ok=True)
+    host_objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(sdir, os.path.splitext(src)[0] + ".san.o")
+        subprocess.check_call(["g++", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
+                               "-I", os.path.join(rocm, "include"), "-I", INCLUDE, "-I", CSRC]
+                              + san + ["-c", os.path.join(CSRC, src), "-o", obj])
+        host_objs.append(obj)
+    tmp = path + ".tmp%d" % os.getpid()
+    subprocess.check_call(["g++", "-shared", "-fsanitize=address,undefined"] + host_objs
+                          + dev_objs + ["-L", os.path.join(rocm, "lib"), "-lamdhip64",
+                                        "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp])
+    os.replace(tmp, path)
+    return path
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -245,7 +245,12 @@ size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t
  * partner softmax to out: in the attention kernel's epilogue for bf16 at every
  * q_block except 192, otherwise in a second kernel enqueued after it.
  * In bf16 the probabilities are rounded to bf16 for the P.V product only; the
- * row sum (and so lse) adds them in fp32. */
+ * row sum (and so lse) adds them in fp32.
+ * Inputs must be finite.  The kernels are built without NaN semantics (maxima
+ * and comparisons assume none), and a masked key still enters the P.V product
+ * with probability 0, so a NaN or infinity anywhere in q, k or v leaves out and
+ * lse unspecified (not a fault) for every query whose query tile visits the key
+ * tile that holds it; other queries are unaffected. */
 na_status na_forward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
                      const na_tensor* k, const na_tensor* v, const na_tensor* out, float* lse,
                      float scale, uint32_t flags, void* workspace, size_t workspace_bytes,

@@ -77,6 +77,20 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer
+    into `path` (for the CPU sanitizer run of the pins; load it with the
+    sanitizer runtime preloaded)."""
+    tmp = path + ".tmp%d" % os.getpid()
+    subprocess.check_call(
+        ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+         "-fno-sanitize-recover=undefined", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC,
+         "-o", tmp, "-lm"]
+    )
+    os.replace(tmp, path)
+    return path
+
+
 _lib = None
 
 
