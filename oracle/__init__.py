@@ -129,6 +129,13 @@ def lib():
                                                      ctypes.c_double, ctypes.c_void_p,
                                                      ctypes.c_int64, ctypes.c_void_p,
                                                      ctypes.c_int32]
+        L.orc_attention_backward_kv_rows.argtypes = [P(_Spec), ctypes.c_int64, ctypes.c_int64,
+                                                     ctypes.c_int64, ctypes.c_int32,
+                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_double, ctypes.c_void_p,
+                                                     ctypes.c_int64, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_int32]
         L.orc_tile_classes.argtypes = [P(_Spec), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                        P(ctypes.c_int64), ctypes.c_int32]
         L.orc_max_threads.restype = ctypes.c_int32
@@ -348,6 +355,29 @@ def attention_backward_dq(workload: dict, q, k, v, dout, scale: float, rows, thr
     if rc != 0:
         raise ValueError("oracle backward rows failed (%d)" % rc)
     return dq
+
+
+def attention_backward_kv(workload: dict, q, k, v, dout, scale: float, keys, threads: int = 0):
+    """fp64 (dk, dv), each [B, H, len(keys), D], of the same gradients for the
+    listed row-major key tokens only (distinct).  Every query whose
+    neighbourhood holds a listed key runs its full row gradient; cheap when
+    the listed keys share few queries (keys of one tile)."""
+    s = spec(workload)
+    qa, dt = _raw(q)
+    ka, dk_ = _raw(k)
+    va, dv_ = _raw(v)
+    ga, dg = _raw(dout)
+    assert dt == dk_ == dv_ == dg, "q, k, v, dout must share a dtype"
+    B, H, N, D = qa.shape
+    keys_a = np.ascontiguousarray(np.asarray(keys, dtype=np.int64))
+    dk = np.empty((B, H, keys_a.shape[0], D), dtype=np.float64)
+    dv = np.empty_like(dk)
+    rc = lib().orc_attention_backward_kv_rows(ctypes.byref(s), B, H, D, dt, _ptr(qa), _ptr(ka),
+                                              _ptr(va), _ptr(ga), float(scale), _ptr(keys_a),
+                                              keys_a.shape[0], _ptr(dk), _ptr(dv), int(threads))
+    if rc != 0:
+        raise ValueError("oracle backward key rows failed (%d)" % rc)
+    return dk, dv
 
 
 def tile_classes(workload: dict, q_block: int, kv_block: int, threads: int = 0):

@@ -552,13 +552,15 @@ int orc_attention(const orc_spec* s, int64_t B, int64_t H, int64_t D, int32_t dt
      dP_ij = dout_i . v_j                         (Eq. 3 is linear in P)
      dz_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')   (softmax Jacobian, Eq. 23)
      dq_i += scale dz_ij k_j,  dk_j += scale dz_ij q_i,  dv_j += P_ij dout_i.
-   dqi receives dq_i (D values, added to); dk / dv (whole slices) may be NULL.
+   dqi receives dq_i (D values, added to) and may be NULL.  dk / dv (the
+   slice's rows, added to) may be NULL; with slot == NULL key j's row is row j,
+   else it is row slot[j] and keys with slot[j] < 0 are not accumulated.
    nb, p, dp: scratch of N entries; qi, gi: scratch of D entries. */
 static void grad_branch(const orc_spec* s, const int64_t* perm, const int64_t* pos, int64_t D,
                         int32_t dtype, const void* q, const void* k, const void* v,
                         const void* dout, double scale, int64_t head, int64_t i, int branch,
-                        double* dqi, double* dk, double* dv, int64_t* nb, double* p, double* dp,
-                        double* qi, double* gi) {
+                        double* dqi, double* dk, double* dv, const int64_t* slot, int64_t* nb,
+                        double* p, double* dp, double* qi, double* gi) {
     /* the log-priors of fixed fusion are constants: they change P, not the
        Jacobian of the softmax with respect to z.  dp holds them until the dP
        values overwrite it. */
@@ -593,10 +595,13 @@ static void grad_branch(const orc_spec* s, const int64_t* perm, const int64_t* p
     for (int64_t a = 0; a < n; ++a) {
         const double dz = p[a] * (dp[a] - delta);
         const int64_t j = head + nb[a] * D;
+        if (dqi)
+            for (int64_t d = 0; d < D; ++d) dqi[d] += scale * dz * load_elem(k, dtype, j + d);
+        const int64_t row = slot ? slot[nb[a]] : nb[a];
+        if (row < 0) continue;
         for (int64_t d = 0; d < D; ++d) {
-            dqi[d] += scale * dz * load_elem(k, dtype, j + d);
-            if (dk) dk[j + d] += scale * dz * qi[d];
-            if (dv) dv[j + d] += p[a] * gi[d];
+            if (dk) dk[row * D + d] += scale * dz * qi[d];
+            if (dv) dv[row * D + d] += p[a] * gi[d];
         }
     }
 }
@@ -606,11 +611,11 @@ static void grad_branch(const orc_spec* s, const int64_t* perm, const int64_t* p
 static void grad_row(const orc_spec* s, const int64_t* perm, const int64_t* pos, int64_t D,
                      int32_t dtype, const void* q, const void* k, const void* v,
                      const void* dout, double scale, int64_t head, int64_t i, double* dqi,
-                     double* dk, double* dv, int64_t* nb, double* p, double* dp, double* qi,
-                     double* gi) {
+                     double* dk, double* dv, const int64_t* slot, int64_t* nb, double* p,
+                     double* dp, double* qi, double* gi) {
     for (int branch = 0; branch < 2; ++branch)
-        grad_branch(s, perm, pos, D, dtype, q, k, v, dout, scale, head, i, branch, dqi, dk, dv, nb,
-                    p, dp, qi, gi);
+        grad_branch(s, perm, pos, D, dtype, q, k, v, dout, scale, head, i, branch, dqi, dk, dv,
+                    slot, nb, p, dp, qi, gi);
 }
 
 /* Every (batch, head) slice is owned by one thread, so the scatter into dk and
@@ -644,7 +649,7 @@ int orc_attention_backward(const orc_spec* s, int64_t B, int64_t H, int64_t D, i
             const int64_t head = bh * N * D;
             for (int64_t i = 0; i < N; ++i)
                 grad_row(s, perm, pos, D, dtype, q, k, v, dout, scale, head, i, dq + head + i * D,
-                         dk, dv, nb, p, dp, qi, gi);
+                         dk + head, dv + head, NULL, nb, p, dp, qi, gi);
         }
         free(gi);
         free(qi);
@@ -691,7 +696,7 @@ int orc_attention_backward_dq_rows(const orc_spec* s, int64_t B, int64_t H, int6
                 continue;
             }
             grad_row(s, perm, pos, D, dtype, q, k, v, dout, scale, bh * N * D, i, out, NULL, NULL,
-                     nb, p, dp, qi, gi);
+                     NULL, nb, p, dp, qi, gi);
         }
         free(gi);
         free(qi);
@@ -702,6 +707,86 @@ int orc_attention_backward_dq_rows(const orc_spec* s, int64_t B, int64_t H, int6
     free(pos);
     free(perm);
     return err ? -2 : 0;
+}
+
+/* Does the neighbourhood (either branch) of query i hold a listed key? */
+static int attends_listed(const orc_spec* s, const int64_t* perm, const int64_t* pos, int64_t i,
+                          const int64_t* slot, int64_t* nb) {
+    for (int branch = 0; branch < 2; ++branch) {
+        const int64_t n = branch_keys(s, perm, pos, i, branch, nb, NULL);
+        for (int64_t a = 0; a < n; ++a)
+            if (slot[nb[a]] >= 0) return 1;
+    }
+    return 0;
+}
+
+/* dk and dv of the same gradients for the listed row-major key tokens only.
+   dk_j and dv_j sum the terms of every query i whose neighbourhood holds j,
+   so each query is tested and those that hold a listed key run the full
+   gradient of their row (its softmax and delta need the whole
+   neighbourhood); the other queries add nothing.  Per-thread partial sums
+   are added at the end. */
+int orc_attention_backward_kv_rows(const orc_spec* s, int64_t B, int64_t H, int64_t D,
+                                   int32_t dtype, const void* q, const void* k, const void* v,
+                                   const void* dout, double scale, const int64_t* keys,
+                                   int64_t nkeys, double* dk, double* dv, int32_t threads) {
+    const int64_t N = orc_num_tokens(s);
+    int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    for (int64_t j = 0; j < N; ++j) slot[j] = -1;
+    for (int64_t a = 0; a < nkeys; ++a) {
+        if (keys[a] < 0 || keys[a] >= N || slot[keys[a]] >= 0) {
+            free(slot);
+            return -2; /* out of range or listed twice */
+        }
+        slot[keys[a]] = a;
+    }
+    int64_t* perm = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (orc_order(s, perm) != 0) {
+        free(perm);
+        free(slot);
+        return -1;
+    }
+    int64_t* pos = invert(perm, N);
+    const int64_t per_head = nkeys * D;
+    for (int64_t t = 0; t < B * H * per_head; ++t) dk[t] = dv[t] = 0.0;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+        double* p = (double*)malloc(sizeof(double) * (size_t)N);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+        double* qi = (double*)malloc(sizeof(double) * (size_t)D);
+        double* gi = (double*)malloc(sizeof(double) * (size_t)D);
+        double* pk = (double*)calloc((size_t)(B * H * per_head), sizeof(double));
+        double* pv = (double*)calloc((size_t)(B * H * per_head), sizeof(double));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < B * H * N; ++t) {
+            const int64_t bh = t / N, i = t % N;
+            if (!attends_listed(s, perm, pos, i, slot, nb)) continue;
+            grad_row(s, perm, pos, D, dtype, q, k, v, dout, scale, bh * N * D, i, NULL,
+                     pk + bh * per_head, pv + bh * per_head, slot, nb, p, dp, qi, gi);
+        }
+#pragma omp critical
+        for (int64_t t = 0; t < B * H * per_head; ++t) {
+            dk[t] += pk[t];
+            dv[t] += pv[t];
+        }
+        free(pv);
+        free(pk);
+        free(gi);
+        free(qi);
+        free(dp);
+        free(p);
+        free(nb);
+    }
+    free(pos);
+    free(perm);
+    free(slot);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -151,6 +151,14 @@ int orc_attention_backward_dq_rows(const orc_spec* s, int64_t B, int64_t H, int6
                                    const void* dout, double scale, const int64_t* rows,
                                    int64_t nrows, double* dq, int32_t threads);
 
+/* dk and dv of the same gradients for the listed row-major key tokens only
+   (distinct, in [0, N)): dk, dv [B][H][nkeys][D] fp64.  Returns 0 on success,
+   -2 for a key out of range or listed twice. */
+int orc_attention_backward_kv_rows(const orc_spec* s, int64_t B, int64_t H, int64_t D,
+                                   int32_t dtype, const void* q, const void* k, const void* v,
+                                   const void* dout, double scale, const int64_t* keys,
+                                   int64_t nkeys, double* dk, double* dv, int32_t threads);
+
 /* Tile classes over the sequence order: cls[qt * nkt + kt] in {0 empty,
    1 partial, 2 full}; nqt = ceil(N/q_block), nkt = ceil(N/kv_block).
    *pairs receives the attended-pair count.  Returns 0 on success. */

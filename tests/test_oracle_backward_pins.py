@@ -150,3 +150,42 @@ def test_backward_dq_rows_subset():
     rows = np.array([0, 7, 31, N - 1])
     sub = oracle.attention_backward_dq(wl, q, k, v, g, 0.4, rows)
     assert np.array_equal(sub, dq[:, :, rows])
+
+
+KV_CASES = [
+    MASKED[3],
+    dict(name="sta_tiled_2x3", B=2, H=3, D=4, dtype="fp32", grid=[6, 8], order="tiled",
+         tile=[2, 4], pattern=dict(kind="sta", tile=[2, 4], window_tiles=[3, 1])),
+    dict(name="pi_separate", B=1, H=2, D=4, dtype="fp32", grid=[40], order="row_major",
+         pattern=dict(kind="band", left=5, right=0, skip=9, skip_mode="separate")),
+    dict(name="pi_fixed_fusion", B=1, H=1, D=4, dtype="fp32", grid=[40], order="row_major",
+         pattern=dict(kind="band", left=5, right=0, skip=9, skip_mode="fixed_fusion",
+                      skip_prior=0.8)),
+]
+
+
+@pytest.mark.parametrize("wl", KV_CASES, ids=[w["name"] for w in KV_CASES])
+def test_backward_kv_rows_subset(wl):
+    """dk and dv of selected keys equal the same rows of the full gradient
+    (up to the order of the fp64 additions: per-thread partial sums)."""
+    B, H = wl["B"], wl["H"]
+    N = W.num_tokens(wl)
+    D = wl["D"]
+    q, k, v, g = (_rand((B, H, N, D), s) for s in (71, 72, 73, 74))
+    _, dk, dv = oracle.attention_backward(wl, q, k, v, g, 0.4)
+    keys = np.array([N - 1, 0, 5, N // 2])
+    sk, sv = oracle.attention_backward_kv(wl, q, k, v, g, 0.4, keys)
+    np.testing.assert_allclose(sk, dk[:, :, keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sv, dv[:, :, keys], rtol=0, atol=1e-12)
+    sk, sv = oracle.attention_backward_kv(wl, q, k, v, g, 0.4, np.arange(N))
+    np.testing.assert_allclose(sk, dk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sv, dv, rtol=0, atol=1e-12)
+
+
+def test_backward_kv_rows_rejects_bad_keys():
+    wl = MASKED[3]
+    N = W.num_tokens(wl)
+    q, k, v, g = (_rand((1, 1, N, 8), s) for s in (81, 82, 83, 84))
+    for keys in ([0, 3, 3], [N], [-1]):
+        with pytest.raises(ValueError):
+            oracle.attention_backward_kv(wl, q, k, v, g, 0.4, np.array(keys))
