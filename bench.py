@@ -120,9 +120,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--q-block", type=int, default=0,
-                    help="query tile; 0 = the forward pass takes 384 at head_dim 128 when every "
-                         "visited tile pair is full at 384 (sliding-tile maps: each staged K/V "
-                         "tile then serves 1.5x the queries), else the library default")
+                    help="query tile; 0 = the forward pass takes the launch of "
+                         "na.forward_launch (384 at head_dim 128 in bf16; 8x8 patch order and 64 "
+                         "at head_dim 64 for 2-D windows in row-major order), the backward pass "
+                         "the library default")
     ap.add_argument("--permute-passes", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -139,8 +140,8 @@ def main():
                          "speedup bounds")
     ap.add_argument("--plan-times", action="store_true",
                     help="only time host plan creation (tile map, CSR, masks; no device upload) "
-                         "for the five named workloads at their benchmark query tiles: median of "
-                         "3, one JSON line each (runs without a GPU)")
+                         "for the five named workloads in their forward launch: median of 3, one "
+                         "JSON line each (runs without a GPU)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the row-permute kernel over 268,435,456 bytes (read once, "
                          "written once): the known-size copy that calibrates HBM counters")
@@ -156,11 +157,9 @@ def main():
         from dimensional_sparse_local_amd import na
         from dimensional_sparse_local_amd import workloads as W
 
-        for name, q_block in (("na2d_fp32", 0), ("na2d_bf16", 64), ("sta3d_bf16", 384),
-                              ("hilbert_band_bf16", 0), ("causal1d_bf16", 0)):
-            wl = W.CONFIGS[name]
-            if name == "na2d_bf16":   # the benchmark's internal 8x8 patch order
-                wl = W.scaled(wl, order="tiled", tile=[8, 8])
+        for name in ("na2d_fp32", "na2d_bf16", "sta3d_bf16", "hilbert_band_bf16",
+                     "causal1d_bf16"):
+            wl, q_block = na.forward_launch(W.CONFIGS[name])
             ts = []
             for _ in range(3):
                 t0 = time.perf_counter()
@@ -196,20 +195,11 @@ def main():
     B, H, D = int(wl["B"]), int(wl["H"]), int(wl["D"])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q_block = args.q_block
-    internal = None
-    if q_block == 0 and args.which == "forward" and D == 128 and wl["dtype"] == "bf16":
-        if na.Plan(wl, host_only=True, q_block=384).stats["n_partial"] == 0:
-            q_block = 384
-    if (q_block == 0 and args.which == "forward" and D == 64 and wl["dtype"] == "bf16"
-            and wl["order"] == "row_major" and len(wl["grid"]) == 2
-            and wl["pattern"]["kind"] in ("na", "sa")):
-        # the token order inside the kernel is free (q, k, v, out stay row-major):
-        # 8x8 patches make the visited tile pairs denser, 64-query tiles give
-        # the short walks more workgroups
-        internal = dict(order="tiled", tile=[8, 8])
-        q_block = 64
-    plan = na.Plan(W.scaled(wl, **internal) if internal else wl, q_block=q_block)
+    kernel_wl, q_block = wl, args.q_block
+    if q_block == 0 and args.which == "forward":
+        kernel_wl, q_block = na.forward_launch(wl)
+    internal = kernel_wl is not wl
+    plan = na.Plan(kernel_wl, q_block=q_block)
     flops = plan.effective_flops(B, H)
     q, k, v = W.make_qkv(wl, device=dev)
     scale = W.default_scale(wl)
@@ -359,7 +349,8 @@ def main():
                    "effective_flops_per_step": flops,
                    "pct_of_peak": round(100.0 * tflops / peak, 2),
                    "permute_passes": bool(args.permute_passes), "pass": args.which,
-                   "internal_order": internal or {"order": wl["order"]}},
+                   "internal_order": ({k: kernel_wl[k] for k in ("order", "tile")} if internal
+                                      else {"order": wl["order"]})},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -627,11 +627,17 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
         }
     };
 
-    auto compute = [&](NaEntry entry, const u32x2* ml, const uint16_t* kl, const uint16_t* vl) {
+    // One K/V tile; mid() runs once the first half's scores are in registers
+    // (the walk issues the next tile's DMA there, so its LDS writes overlap
+    // the softmax and P.V products rather than this tile's K reads).
+    auto compute = [&](NaEntry entry, const u32x2* ml, const uint16_t* kl, const uint16_t* vl,
+                       auto mid) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {   // two 32-key halves of the tile
             f32x4 s[2][QBN];
             scores(hs, entry, ml, kl, s);
+            if (hs == 0) mid();
+
             // online softmax against each row's reference maximum, which moves
             // only for a row with none yet or a lane sum past 2^kSumLog2 (the
             // wave then recomputes the half's scores and takes exact maxima)
@@ -703,10 +709,11 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
                     uint16_t* vn, u32x2* mn) {
         wait_vmem();
         __syncthreads();
-        if (e + 1 < e1) issue(ent_b, tok_n, kn, vn, mn);
-        if (e + 2 < e1) tokens(ent_c, tok_n);
         const NaEntry ent_d = e + 3 < e1 ? load_entry(p.entries + e + 3) : none;
-        compute(ent_a, ml, kl, vl);
+        compute(ent_a, ml, kl, vl, [&]() {
+            if (e + 1 < e1) issue(ent_b, tok_n, kn, vn, mn);
+            if (e + 2 < e1) tokens(ent_c, tok_n);
+        });
         ent_a = ent_b;
         ent_b = ent_c;
         ent_c = ent_d;

@@ -191,6 +191,32 @@ def desc_from_workload(w: dict, q_block: int = 0, kv_block: int = 0) -> Desc:
     return d
 
 
+def forward_launch(w: dict) -> tuple[dict, int]:
+    """(kernel-side workload, query tile) for the forward pass alone, the
+    fastest measured launch of each shape:
+
+    * bf16, head_dim 128, no fixed-fusion bias: 384-query tiles (the 16x16x32
+      MFMA kernel, 48 queries per wave): each staged K/V tile serves 1.5x the
+      queries of a 256-query tile, on full and partial tile pairs alike;
+    * bf16, head_dim 64, 2-D neighbourhood or slide window in row-major order:
+      8x8 patch order inside the kernel (q, k, v, out stay row-major) makes the
+      visited tile pairs denser, and 64-query tiles give the short walks more
+      workgroups;
+    * otherwise the library defaults (the workload as given, query tile 0).
+
+    The gradient kernels take 128- or 256-query tiles: a plan made for the
+    backward pass keeps the defaults."""
+    pat = w["pattern"]
+    bias = pat.get("skip", 0) > 0 and pat.get("skip_mode", "union") == "fixed_fusion"
+    if w.get("dtype", "bf16") == "bf16" and int(w["D"]) == 128 and not bias:
+        return w, 384
+    if (w.get("dtype", "bf16") == "bf16" and int(w["D"]) == 64
+            and w.get("order", "row_major") == "row_major" and len(w["grid"]) == 2
+            and pat["kind"] in ("na", "sa")):
+        return dict(w, order="tiled", tile=[8, 8]), 64
+    return w, 0
+
+
 class Plan:
     """A tile map built once per shape (na_plan_create) and run many times."""
 
