@@ -130,13 +130,16 @@ def _sample_rows(wl, n_random, seed=0):
     return np.array(sorted(corners | set(int(x) for x in rnd)), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["sta3d_bf16", "causal1d_bf16"])
-def test_backward_full_size(name):
-    """Full-size workloads, launched as the benchmark launches them: dq on
-    sampled query rows against the oracle; dk and dv through identities that
-    hold at any size (adding one vector to every key leaves the attention
-    unchanged, so sum_j dk_j = 0; the rows of P sum to one, so
-    sum_j dv_j = sum_i dout_i)."""
+def _compare(label, got, want):
+    got = got.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), label
+    rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
+    mx = np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30)
+    print("  %s: rel-L2 %.2e max %.2e" % (label, rel, mx), flush=True)
+    assert rel <= REL_L2 and mx <= MAX_REL, "%s: rel-L2 %.3e, max %.3e" % (label, rel, mx)
+
+
+def _full_size_grads(name):
     na = _na()
     wl = W.CONFIGS[name]
     print("case %s (full size)" % name, flush=True)
@@ -147,16 +150,60 @@ def test_backward_full_size(name):
     out, lse = plan.forward(q, k, v, scale=scale)
     dq, dk, dv = plan.backward(q, k, v, out, lse, g, scale=scale)
     torch.cuda.synchronize()
-    rows = _sample_rows(wl, 24, seed=wl["seed"])
-    heads = [0, int(wl["H"]) - 1]
-    sub = lambda x: x[:, heads].contiguous()
-    ref = oracle.attention_backward_dq(wl, sub(q).cpu(), sub(k).cpu(), sub(v).cpu(), sub(g).cpu(),
-                                       scale, rows)
-    got = dq[:, heads][:, :, rows].float().cpu().numpy()
-    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    mx = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
-    print("  dq rows: rel-L2 %.2e max %.2e" % (rel, mx), flush=True)
-    assert rel <= REL_L2 and mx <= MAX_REL
+    return wl, scale, (q, k, v, g), (dq, dk, dv)
+
+
+def _head(x, h):
+    return x[:, h:h + 1].contiguous().cpu()
+
+
+def test_backward_full_size_causal():
+    """The 1-D causal window at full size (32768 tokens, 4096 keys), launched
+    as the benchmark launches its backward pass: dq, dk and dv of the last
+    head compared element by element, every row, and dq of the first head on
+    sampled rows."""
+    wl, scale, (q, k, v, g), (dq, dk, dv) = _full_size_grads("causal1d_bf16")
+    N, h = W.num_tokens(wl), int(wl["H"]) - 1
+    args = [_head(x, h) for x in (q, k, v, g)]
+    all_rows = np.arange(N, dtype=np.int64)
+    ref_dq = oracle.attention_backward_dq(wl, *args, scale, all_rows)
+    _compare("dq head %d" % h, dq[:, h:h + 1], ref_dq)
+    ref_dk, ref_dv = oracle.attention_backward_kv(wl, *args, scale, all_rows)
+    _compare("dk head %d" % h, dk[:, h:h + 1], ref_dk)
+    _compare("dv head %d" % h, dv[:, h:h + 1], ref_dv)
+    rows = _sample_rows(wl, 64, seed=wl["seed"])
+    ref0 = oracle.attention_backward_dq(wl, *[_head(x, 0) for x in (q, k, v, g)], scale, rows)
+    _compare("dq head 0 rows", dq[:, 0:1][:, :, rows], ref0)
+
+
+def test_backward_full_size_sta3d():
+    """The 3-D sliding-tile map at full size (30x48x80, 3x5x7 tiles of
+    6x8x8), launched as the benchmark launches its backward pass.  dq: sampled
+    rows (grid corners and random rows) of the first and last heads.  dk and
+    dv: element by element on 16 random key rows from each of the two corner
+    tiles of the grid, for one head.  The oracle's cost for a key is every
+    query that attends it, each with its whole row: a corner tile is attended
+    by 24 query tiles (2x3x4), an interior one by 105.  Over all keys, the
+    identities sum_j dk_j = 0 (adding one vector to every key leaves the
+    attention unchanged) and sum_j dv_j = sum_i dout_i (the rows of P sum to
+    one)."""
+    wl, scale, (q, k, v, g), (dq, dk, dv) = _full_size_grads("sta3d_bf16")
+    N, H = W.num_tokens(wl), int(wl["H"])
+    for h in (0, H - 1):
+        rows = _sample_rows(wl, 24, seed=wl["seed"] + h)
+        ref = oracle.attention_backward_dq(wl, *[_head(x, h) for x in (q, k, v, g)], scale, rows)
+        _compare("dq head %d rows" % h, dq[:, h:h + 1][:, :, rows], ref)
+    # the sequence order runs tile by tile (384 tokens per 6x8x8 tile)
+    order = oracle.order(wl)
+    tile = 6 * 8 * 8
+    rng = np.random.default_rng(wl["seed"] + 7)
+    keys = np.concatenate([order[t0 + rng.choice(tile, 16, replace=False)]
+                           for t0 in (0, N - tile)]).astype(np.int64)
+    h = H // 2
+    ref_dk, ref_dv = oracle.attention_backward_kv(wl, *[_head(x, h) for x in (q, k, v, g)], scale,
+                                                  keys)
+    _compare("dk head %d key rows" % h, dk[:, h:h + 1][:, :, keys], ref_dk)
+    _compare("dv head %d key rows" % h, dv[:, h:h + 1][:, :, keys], ref_dv)
     sdv = dv.double().sum(dim=2)
     sg = g.double().sum(dim=2)
     e_dv = (torch.linalg.norm(sdv - sg) / torch.linalg.norm(sg)).item()

@@ -6,9 +6,12 @@ probability to bf16 (round to nearest even) for the P.V product only; the row
 sum adds the fp32 probabilities, so lse carries fp32 rounding of the logits,
 the exponentials, the sum and the log: a few ulps of |scale * q.k|, far inside
 1e-3.
-Small cases compare every element; the full-size workloads compare sampled
-query rows (all grid corners plus seeded random rows), launched exactly as the
-benchmark launches them.
+Small cases compare every element.  The full-size workloads run in the
+launch the benchmark times (na.forward_launch): every element where the oracle
+finishes in seconds (both 2-D neighbourhood sizes, the Hilbert band, the 1-D
+causal window), else, for the 3-D sliding-tile maps, one seeded random query
+from each query tile of the plan plus the grid corners, drawn afresh for every
+(batch, head).
 """
 import math
 import os
@@ -64,16 +67,6 @@ def _run(wl, rows=None, q_block=0, permute_passes=False, seed=None):
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.attention(wl, q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
     return _check(wl, out, lse, ref_out, ref_lse, rows=rows, label=wl["name"])
-
-
-def _sample_rows(wl, n_random, seed=0):
-    grid = wl["grid"]
-    corners = set()
-    for c in np.ndindex(*([2] * len(grid))):
-        corners.add(int(np.ravel_multi_index([(g - 1) * b for g, b in zip(grid, c)], grid)))
-    rng = np.random.default_rng(seed)
-    rnd = rng.choice(W.num_tokens(wl), size=n_random, replace=False)
-    return np.array(sorted(corners | set(int(x) for x in rnd)), dtype=np.int64)
 
 
 # ---------------------------------------------------------------------------
@@ -162,19 +155,9 @@ def test_d128_q256(wl):
 
 @pytest.mark.parametrize("wl", D128_QB256, ids=[w["name"] for w in D128_QB256])
 def test_d128_q384(wl):
-    """Twelve waves of 32 queries (three per SIMD) on the same cases."""
+    """Eight waves of 48 queries (three 16-query MFMA blocks each) on the same
+    cases."""
     _run(wl, q_block=384)
-
-
-@pytest.mark.parametrize("name", ["sta3d_bf16", "sta3d_causal_t_bf16"])
-def test_full_size_q384(name):
-    """The sliding-tile workloads as the benchmark launches their forward pass:
-    384-query tiles, every visited tile pair full."""
-    wl = W.ALL[name]
-    from dimensional_sparse_local_amd import na
-
-    assert na.Plan(wl, host_only=True, q_block=384).stats["n_partial"] == 0
-    _run(wl, rows=_sample_rows(wl, 24, seed=wl["seed"] + 1), q_block=384)
 
 
 def test_hilbert_permute_passes():
@@ -285,18 +268,85 @@ def test_abi_rejects_bad_tensors():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads: sampled rows, launched as the benchmark launches them
+# full-size workloads, launched as the benchmark launches their forward pass
+# (na.forward_launch): every element where the oracle finishes in seconds,
+# else a stratified sample drawn afresh for every (batch, head)
 # ---------------------------------------------------------------------------
 
-FULL = [("na2d_fp32", None), ("na2d_bf16", None), ("sta3d_bf16", 24),
-        ("hilbert_band_bf16", 192), ("causal1d_bf16", 96)]
+def _launched(wl):
+    na = _na()
+    kwl, q_block = na.forward_launch(wl)
+    print("case %s launched as order=%s q_block=%d" % (wl["name"], kwl["order"], q_block),
+          flush=True)
+    plan = na.Plan(kwl, q_block=q_block)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    scale = W.default_scale(wl)
+    out, lse = plan.forward(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    return plan, q, k, v, scale, out, lse
 
 
-@pytest.mark.parametrize("name,n_rows", FULL, ids=[f[0] for f in FULL])
-def test_full_size(name, n_rows):
+@pytest.mark.parametrize("name", ["na2d_fp32", "na2d_bf16", "hilbert_band_bf16",
+                                  "causal1d_bf16"])
+def test_full_size_every_element(name):
+    """Every output and lse element of every (batch, head)."""
     wl = W.CONFIGS[name]
-    rows = None if n_rows is None else _sample_rows(wl, n_rows, seed=wl["seed"])
-    _run(wl, rows=rows)
+    plan, q, k, v, scale, out, lse = _launched(wl)
+    ref_out, ref_lse = oracle.attention(wl, q.cpu(), k.cpu(), v.cpu(), scale)
+    err = _check(wl, out, lse, ref_out, ref_lse, label=name)
+    print("  every element: max-abs %.2e" % err, flush=True)
+
+
+def test_full_size_hilbert_permute_passes():
+    """The Hilbert band with the row gathers as separate passes (q, k, v into
+    curve order, out back to row-major): every element."""
+    na = _na()
+    wl = W.CONFIGS["hilbert_band_bf16"]
+    plan = na.Plan(wl)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    scale = W.default_scale(wl)
+    out, lse = plan.forward(q, k, v, scale=scale, permute_passes=True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention(wl, q.cpu(), k.cpu(), v.cpu(), scale)
+    _check(wl, out, lse, ref_out, ref_lse, label="hilbert_band_bf16 passes")
+
+
+def _tile_strata(plan, n_tokens, rng, grid):
+    """One random query from every query tile of the plan (through its token
+    order) plus the grid's corners, as row-major token indices."""
+    order = plan.order()
+    qb = plan.stats["q_block"]
+    rows = set()
+    for t0 in range(0, n_tokens, qb):
+        rows.add(int(order[t0 + rng.integers(0, min(qb, n_tokens - t0))]))
+    for c in np.ndindex(*([2] * len(grid))):
+        rows.add(int(np.ravel_multi_index([(g - 1) * b for g, b in zip(grid, c)], grid)))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["sta3d_bf16", "sta3d_causal_t_bf16"])
+def test_full_size_stratified(name):
+    """The 3-D sliding-tile workloads: for every (batch, head) its own draw
+    of one query from each of the plan's query tiles (300 tiles of 384 at
+    30x48x80) plus the eight grid corners, each compared element by element
+    with the oracle on that head alone."""
+    wl = W.ALL[name]
+    plan, q, k, v, scale, out, lse = _launched(wl)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    N = W.num_tokens(wl)
+    rng = np.random.default_rng(wl["seed"] + 100)
+    one = W.scaled(wl, B=1, H=1)
+    n_rows = 0
+    for b in range(int(wl["B"])):
+        for h in range(int(wl["H"])):
+            rows = _tile_strata(plan, N, rng, wl["grid"])
+            n_rows += rows.size
+            sl = lambda x: x[b:b + 1, h:h + 1].contiguous()
+            ref_out, ref_lse = oracle.attention(one, sl(qc), sl(kc), sl(vc), scale, rows=rows)
+            _check(one, out[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ref_out, ref_lse,
+                   rows=rows, label="%s b=%d h=%d" % (name, b, h))
+    print("  %d rows over %d heads" % (n_rows, int(wl["B"]) * int(wl["H"])), flush=True)
+    assert n_rows >= plan.stats["n_q_tiles"] * int(wl["B"]) * int(wl["H"])
 
 
 # ---------------------------------------------------------------------------
@@ -357,11 +407,6 @@ def test_gna_small(wl):
     _run(wl)
 
 
-def test_block_causal_video_full_size():
-    wl = W.GNA["sta3d_causal_t_bf16"]
-    _run(wl, rows=_sample_rows(wl, 24, seed=wl["seed"]))
-
-
 # 64-query tiles (head_dim 64): one tile per 64-position window of HWA
 Q64 = [w for w in SMALL_BF16 if w["D"] == 64] + [
     W.scaled(W.HILBERT_PAGE["hwa96_bf16"], B=2), W.scaled(W.HILBERT_PAGE["hna56_bf16"], B=2),
@@ -370,12 +415,4 @@ Q64 = [w for w in SMALL_BF16 if w["D"] == 64] + [
 
 @pytest.mark.parametrize("wl", Q64, ids=[w["name"] for w in Q64])
 def test_query_block_64(wl):
-    _run(wl, q_block=64)
-
-
-def test_full_size_na2d_as_benched():
-    """The 64x64 13x13 neighbourhood workload as the benchmark launches its
-    forward pass: 8x8 patch order inside the kernel, 64-query tiles, every
-    element compared (inputs and outputs stay in row-major order)."""
-    wl = W.scaled(W.CONFIGS["na2d_bf16"], order="tiled", tile=[8, 8])
     _run(wl, q_block=64)
