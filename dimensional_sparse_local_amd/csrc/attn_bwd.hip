@@ -20,6 +20,8 @@
 // products; accumulation is fp32.
 #include "attn_common.h"
 
+#include <mutex>
+
 namespace {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -671,4 +673,33 @@ int na_bwd_launch(const NaBwdParams& p, int head_dim, bool fusion, bool with_del
     if (head_dim == 64)
         return fusion ? launch_bwd<64, true>(p, with_delta, st) : launch_bwd<64, false>(p, with_delta, st);
     return (int)hipErrorInvalidValue;
+}
+
+// ---- fixed device scratch of na_backward_noalloc ----------------------------
+// The delta rows (fp32 [B][H][N]) of the no-allocation backward live in this
+// array of the code object's static data: one copy per GPU, at its own address
+// on each, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in): it takes the device
+// address from hipGetSymbolAddress, once per device with that device current.
+static __device__ __align__(256) float scratch[NA_BACKWARD_NOALLOC_MAX_BYTES / sizeof(float)];
+
+int na_bwd_scratch(void** ptr, size_t* bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* per_device[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void* addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (!addr) return (int)hipErrorInvalidSymbol;
+        per_device[dev] = addr;
+    }
+    *ptr = per_device[dev];
+    *bytes = sizeof(scratch);
+    return 0;
 }

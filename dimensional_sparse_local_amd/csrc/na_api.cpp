@@ -537,6 +537,49 @@ na_status na_backward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, con
     return NA_OK;
 }
 
+na_status na_backward_noalloc(na_plan_t p, int64_t B, int64_t H, const na_tensor* q,
+                              const na_tensor* k, const na_tensor* v, const na_tensor* out,
+                              const na_tensor* dout, const float* lse, const na_tensor* dq,
+                              const na_tensor* dk, const na_tensor* dv, float scale,
+                              void* stream) {
+    if (!p) {
+        na_set_error("plan is NULL");
+        return NA_ERR_INVALID_ARG;
+    }
+    if (B < 1 || H < 1) {
+        na_set_error("B and H must be >= 1");
+        return NA_ERR_INVALID_ARG;
+    }
+    // (in double: no overflow; the limit is a multiple of 256, so this is
+    // na_backward_workspace_bytes(p, B, H) <= the limit)
+    if ((double)B * (double)H * (double)p->n_tokens * sizeof(float) >
+        (double)NA_BACKWARD_NOALLOC_MAX_BYTES) {
+        na_set_error("na_backward_noalloc: B * H * N = %lld * %lld * %lld delta rows exceed the "
+                     "fixed scratch of %u bytes (%u rows); use na_backward with a workspace",
+                     (long long)B, (long long)H, (long long)p->n_tokens,
+                     (unsigned)NA_BACKWARD_NOALLOC_MAX_BYTES,
+                     (unsigned)(NA_BACKWARD_NOALLOC_MAX_BYTES / sizeof(float)));
+        return NA_ERR_INVALID_ARG;
+    }
+    if (!p->on_device) {
+        na_set_error("plan was built host-only and cannot run");
+        return NA_ERR_PLAN_MISMATCH;
+    }
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != p->device) {
+        na_set_error("plan lives on device %d, current device is %d", p->device, cur);
+        return NA_ERR_PLAN_MISMATCH;
+    }
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    const int rc = na_bwd_scratch(&ws, &ws_bytes);
+    if (rc != 0) {
+        na_set_error("device scratch lookup failed: %s", hip_err((hipError_t)rc));
+        return NA_ERR_DEVICE;
+    }
+    return na_backward(p, B, H, q, k, v, out, dout, lse, dq, dk, dv, scale, ws, ws_bytes, stream);
+}
+
 na_status na_permute(na_plan_t p, int64_t B, int64_t H, const na_tensor* in, const na_tensor* out,
                      int32_t inverse, void* stream) {
     if (!p) {

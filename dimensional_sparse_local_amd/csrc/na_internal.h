@@ -179,6 +179,9 @@ bool na_bwd_supported(int dtype, int head_dim, int q_block, int kv_block);
 // fusion = the fixed-fusion (logit bias) variants; with_delta = false skips the
 // row sums (the caller has written p.delta).
 int na_bwd_launch(const NaBwdParams& p, int head_dim, bool fusion, bool with_delta, void* stream);
+// Device address and size of this GPU's fixed delta scratch (attn_bwd.hip),
+// looked up once per device; 0 or a hipError_t.
+int na_bwd_scratch(void** ptr, size_t* bytes);
 
 // Returns false if no variant exists for (dtype, head_dim, q_block, kv_block);
 // fusion = the fixed-fusion (logit bias) variant.

@@ -21,6 +21,7 @@ NA_BOUND_CLAMP, NA_BOUND_TRUNCATE = 0, 1
 NA_BF16, NA_F32 = 0, 1
 NA_PLAN_HOST_ONLY = 1
 NA_FWD_PERMUTE_PASSES = 1
+NA_BACKWARD_NOALLOC_MAX_BYTES = 16 << 20
 
 ORDERS = {"row_major": NA_ORDER_ROW_MAJOR, "tiled": NA_ORDER_TILED, "hilbert": NA_ORDER_HILBERT}
 NA_SKIP_UNION, NA_SKIP_FIXED_FUSION, NA_SKIP_SEPARATE = 0, 1, 2
@@ -69,7 +70,7 @@ _STATUS = {NA_ERR_INVALID_ARG: "invalid argument", NA_ERR_UNSUPPORTED: "unsuppor
            NA_ERR_PLAN_MISMATCH: "plan mismatch"}
 
 _lib = None
-ABI_VERSION = 4  # NA_ABI_VERSION of include/na.h that Desc mirrors
+ABI_VERSION = 5  # NA_ABI_VERSION of include/na.h that Desc mirrors
 
 
 def lib():
@@ -97,13 +98,17 @@ def lib():
         L.na_backward.argtypes = [vp, i64, i64, P(Tensor), P(Tensor), P(Tensor), P(Tensor),
                                   P(Tensor), vp, P(Tensor), P(Tensor), P(Tensor), ctypes.c_float,
                                   vp, ctypes.c_size_t, vp]
+        L.na_backward_noalloc.argtypes = [vp, i64, i64, P(Tensor), P(Tensor), P(Tensor),
+                                          P(Tensor), P(Tensor), vp, P(Tensor), P(Tensor),
+                                          P(Tensor), ctypes.c_float, vp]
         L.na_status_string.argtypes = [ctypes.c_int]
         L.na_status_string.restype = ctypes.c_char_p
         L.na_last_error.restype = ctypes.c_char_p
         L.na_abi_version.restype = ctypes.c_int32
         for f in ("na_plan_create", "na_plan_destroy", "na_plan_get_stats", "na_plan_get_bounds",
                   "na_plan_get_classes",
-                  "na_plan_get_order", "na_forward", "na_permute", "na_backward"):
+                  "na_plan_get_order", "na_forward", "na_permute", "na_backward",
+                  "na_backward_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         if L.na_abi_version() != ABI_VERSION:
             raise RuntimeError("libna.so has ABI version %d, this binding expects %d (rebuild)"
@@ -368,6 +373,33 @@ class Plan:
                                  *[ctypes.byref(t) for t in ts[5:]], float(scale),
                                  ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
                                  ctypes.c_void_p(stream)))
+        return dq, dk, dv
+
+    def backward_noalloc(self, q, k, v, out, lse, dout, grads, scale=None, stream=None):
+        """na_backward_noalloc: the gradients into the caller's (dq, dk, dv)
+        with the library's fixed per-GPU scratch (B * H * N <= 4,194,304);
+        nothing is allocated.  Calls that overlap on one GPU race."""
+        import torch
+
+        B, H = int(q.shape[0]), int(q.shape[1])
+        _same_bh(B, H, k=k, v=v, out=out, dout=dout)
+        if len(grads) != 3:
+            raise ValueError("grads must be (dq, dk, dv)")
+        _same_bh(B, H, dq=grads[0], dk=grads[1], dv=grads[2])
+        if (lse.dtype != torch.float32 or not lse.is_contiguous()
+                or tuple(lse.shape) != (B, H, self.n_tokens)):
+            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.head_dim)
+        dq, dk, dv = grads
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        ts = [self._tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"),
+                                              (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+        _check(lib().na_backward_noalloc(self._h, B, H, *[ctypes.byref(t) for t in ts[:5]],
+                                         ctypes.c_void_p(lse.data_ptr()),
+                                         *[ctypes.byref(t) for t in ts[5:]], float(scale),
+                                         ctypes.c_void_p(stream)))
         return dq, dk, dv
 
     def permute(self, x, inverse=False, out=None, stream=None):

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define NA_ABI_VERSION 4
+#define NA_ABI_VERSION 5
 
 typedef enum {
     NA_OK = 0,
@@ -287,6 +287,30 @@ na_status na_backward(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
                       const na_tensor* dout, const float* lse, const na_tensor* dq,
                       const na_tensor* dk, const na_tensor* dv, float scale, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* Size of the fixed device scratch of na_backward_noalloc: 16 MiB per GPU,
+ * the delta rows of B * H * N <= 4,194,304 queries. */
+#define NA_BACKWARD_NOALLOC_MAX_BYTES (16u << 20)
+
+/* na_backward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, the same kernels and results.  Its
+ * delta rows go to a fixed scratch array in the library's static device data,
+ * one per GPU, held until the process ends; the entry point calls no
+ * hipMalloc, hipFree or allocating library routine.  Every element of the
+ * scratch is written before it is read, so nothing needs clearing between
+ * calls.  Calls on one GPU share that GPU's scratch: two calls that overlap in
+ * time on one GPU (different streams, or host threads without ordering) race
+ * and give wrong gradients; order them on one stream.  Returns
+ * NA_ERR_INVALID_ARG when na_backward_workspace_bytes(plan, B, H) exceeds
+ * NA_BACKWARD_NOALLOC_MAX_BYTES (checked before any device call), NA_ERR_DEVICE
+ * if the scratch address cannot be found, and otherwise what na_backward
+ * returns for the same arguments. */
+na_status na_backward_noalloc(na_plan_t plan, int64_t B, int64_t H, const na_tensor* q,
+                              const na_tensor* k, const na_tensor* v, const na_tensor* out,
+                              const na_tensor* dout, const float* lse, const na_tensor* dq,
+                              const na_tensor* dk, const na_tensor* dv, float scale,
+                              void* stream);
 
 /* Row gather along the plan's order: out[b, h, p, :] = in[b, h, perm[p], :]
  * (inverse = 0) or out[b, h, perm[p], :] = in[b, h, p, :] (inverse = 1), for

@@ -7,6 +7,7 @@ import re
 import pytest
 
 from dimensional_sparse_local_amd import na
+from dimensional_sparse_local_amd import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 pytestmark = pytest.mark.skipif(not os.path.exists(na._LIB_PATH), reason="libna.so not built")
@@ -28,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = na.lib()
-    assert lib.na_abi_version() == na.ABI_VERSION == 4
+    assert lib.na_abi_version() == na.ABI_VERSION == 5
     for s in range(6):
         assert lib.na_status_string(s)
     assert lib.na_status_string(99) == b"unknown status"
@@ -130,3 +131,20 @@ def test_permute_rejects_small_out():
     torch, plan, mk = _bh_case()
     with pytest.raises(ValueError, match="out"):
         plan.permute(mk(2, 3), out=mk(2, 2))
+
+
+def test_backward_noalloc_refuses_before_device_work():
+    """The scratch limit and the plan checks of na_backward_noalloc come
+    before any HIP call, so a host-only plan shows them without a GPU."""
+    L = na.lib()
+    assert L.na_backward_noalloc(None, 1, 1, *([None] * 9), 0.1, None) == na.NA_ERR_INVALID_ARG
+    limit_rows = na.NA_BACKWARD_NOALLOC_MAX_BYTES // 4
+    big = na.Plan(W.scaled(W.CONFIGS["causal1d_bf16"], B=2, H=3, D=64,
+                           grid=[limit_rows // 6 + 1], pattern=dict(kind="band", left=3, right=0)),
+                  host_only=True)
+    st = L.na_backward_noalloc(big._h, 2, 3, *([None] * 9), 0.1, None)
+    assert st == na.NA_ERR_INVALID_ARG
+    assert b"scratch" in L.na_last_error()
+    st = L.na_backward_noalloc(big._h, 1, 3, *([None] * 9), 0.1, None)   # fits: 3 * N rows
+    assert st == na.NA_ERR_PLAN_MISMATCH
+    assert L.na_backward_noalloc(big._h, 0, 3, *([None] * 9), 0.1, None) == na.NA_ERR_INVALID_ARG
