@@ -121,10 +121,13 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--q-block", type=int, default=0,
                     help="query tile; 0 = the forward pass takes the launch of "
-                         "na.forward_launch (384 at head_dim 128 in bf16; 8x8 patch order and 64 "
-                         "at head_dim 64 for 2-D windows in row-major order), the backward pass "
-                         "the library default")
+                         "na.forward_launch (384 with the split tail at head_dim 128 in bf16; 8x8 "
+                         "patch order and 64 at head_dim 64 for 2-D windows in row-major order), "
+                         "the backward pass the library default")
     ap.add_argument("--permute-passes", action="store_true")
+    ap.add_argument("--no-split-tail", action="store_true",
+                    help="run the forward without NA_FWD_SPLIT_TAIL even where its launch "
+                         "takes it")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=("forward", "backward", "permute"),
@@ -159,7 +162,7 @@ def main():
 
         for name in ("na2d_fp32", "na2d_bf16", "sta3d_bf16", "hilbert_band_bf16",
                      "causal1d_bf16"):
-            wl, q_block = na.forward_launch(W.CONFIGS[name])
+            wl, q_block, _ = na.forward_launch(W.CONFIGS[name])
             ts = []
             for _ in range(3):
                 t0 = time.perf_counter()
@@ -195,9 +198,10 @@ def main():
     B, H, D = int(wl["B"]), int(wl["H"]), int(wl["D"])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    kernel_wl, q_block = wl, args.q_block
+    kernel_wl, q_block, split = wl, args.q_block, False
     if q_block == 0 and args.which == "forward":
-        kernel_wl, q_block = na.forward_launch(wl)
+        kernel_wl, q_block, split = na.forward_launch(wl)
+    split = split and not args.no_split_tail
     internal = kernel_wl is not wl
     plan = na.Plan(kernel_wl, q_block=q_block)
     flops = plan.effective_flops(B, H)
@@ -206,10 +210,16 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((B, H, plan.n_tokens), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    log("bench: %s plan %s" % (name, plan.stats))
+    # the forward's workspace (permute passes, split tail), allocated once
+    flags = ((na.NA_FWD_PERMUTE_PASSES if args.permute_passes else 0)
+             | (na.NA_FWD_SPLIT_TAIL if split else 0))
+    ws_bytes = int(na.lib().na_forward_workspace_bytes(plan._h, B, H, flags))
+    fwd_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    log("bench: %s plan %s split_tail=%s workspace=%d" % (name, plan.stats, split, ws_bytes))
 
     def step():
-        plan.forward(q, k, v, out=out, lse=lse, scale=scale, permute_passes=args.permute_passes)
+        plan.forward(q, k, v, out=out, lse=lse, scale=scale, permute_passes=args.permute_passes,
+                     split_tail=split, workspace=fwd_ws)
 
     if args.which == "permute":
         if wl["order"] == "row_major" or internal:
@@ -348,7 +358,8 @@ def main():
                    "attended_pairs_per_head": plan.stats["attended_pairs"],
                    "effective_flops_per_step": flops,
                    "pct_of_peak": round(100.0 * tflops / peak, 2),
-                   "permute_passes": bool(args.permute_passes), "pass": args.which,
+                   "permute_passes": bool(args.permute_passes), "split_tail": split,
+                   "pass": args.which,
                    "internal_order": ({k: kernel_wl[k] for k in ("order", "tile")} if internal
                                       else {"order": wl["order"]})},
         "roofline": roof,

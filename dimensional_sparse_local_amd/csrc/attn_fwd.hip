@@ -494,7 +494,10 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     const int q16 = lane & 15, g = lane >> 4;
     const int cg = 2 * (g & 1) + (g >> 1);
 
-    const int wg = xcd_remap(blockIdx.x, p.n_wg);
+    // whole tile, or one share of a tail tile's walk (split tail)
+    const bool part_mode = (int)blockIdx.x >= p.n_main;
+    const int part = (int)blockIdx.x - p.n_main;
+    const int wg = part_mode ? p.n_main + part / p.n_split : xcd_remap(blockIdx.x, p.n_main);
     const int qt = wg % p.n_q_tiles;
     const int bh = wg / p.n_q_tiles;
     const int b = bh / p.heads, h = bh % p.heads;
@@ -692,7 +695,12 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     };
 
     // ---- pipelined walk over the CSR row (as in the 32-query kernel) -----------
-    const int e0 = cload(p.row_ptr + qt), e1 = cload(p.row_ptr + qt + 1);
+    int e0 = cload(p.row_ptr + qt), e1 = cload(p.row_ptr + qt + 1);
+    if (part_mode) {
+        const int len = e1 - e0, j = part % p.n_split;
+        e1 = e0 + (len * (j + 1)) / p.n_split;
+        e0 = e0 + (len * j) / p.n_split;
+    }
     const NaEntry none = {0, -1};
     NaEntry ent_a = none, ent_b = none, ent_c = none;
     int tok_n[IPW];
@@ -724,6 +732,19 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     }
 
     // ---- epilogue -----------------------------------------------------------------
+    if (part_mode) {   // unnormalised share: O, reference maximum, row sum
+#pragma unroll
+        for (int qb = 0; qb < QBN; ++qb) {
+            const float l_tot = quad_sum(l_run[qb]);
+            const int row = wave * (16 * QBN) + 16 * qb + q16;
+            float* po = p.part_o + ((int64_t)part * QB + row) * D + 4 * g;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) *(f32x4*)(po + 16 * db) = o[db][qb];
+            if (g == 0)
+                *(f32x2*)(p.part_ml + 2 * ((int64_t)part * QB + row)) = f32x2{m_ref[qb], l_tot};
+        }
+        return;
+    }
 #pragma unroll
     for (int qb = 0; qb < QBN; ++qb) {
         const float l_tot = quad_sum(l_run[qb]);
@@ -745,6 +766,57 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
             p.lse[(int64_t)bh * N + qtok] = lse;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split tail: merge the n_split shares of each tail tile's walk.  Share j of
+// row i holds O_j = sum 2^(c s - m_j) v and l_j = sum 2^(c s - m_j) over its
+// keys; with M = max m_j over shares that saw a key,
+//     out_i = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j,
+//     lse_i = (M + log2 sum_j 2^(m_j - M) l_j) ln 2,
+// the same result as one walk over all the keys.  Four columns per thread.
+// ---------------------------------------------------------------------------
+template <int D, int QB>
+__global__ __launch_bounds__(256) void attn_fwd_combine(NaAttnParams p) {
+    constexpr int TPR = D / 4;         // threads per row
+    constexpr int RPB = 256 / TPR;     // rows per block
+    const int gr = blockIdx.x * RPB + (int)threadIdx.x / TPR;
+    const int c4 = (int)threadIdx.x % TPR;
+    if (gr >= (p.n_wg - p.n_main) * QB) return;
+    const int tt = gr / QB, row = gr % QB;
+    const int wg = p.n_main + tt;
+    const int qt = wg % p.n_q_tiles, bh = wg / p.n_q_tiles;
+    const int b = bh / p.heads, h = bh % p.heads;
+    const int qpos = qt * QB + row;
+    if (qpos >= p.n_tokens) return;
+    const int64_t first = (int64_t)tt * p.n_split * QB + row;   // share 0 of this row
+    float M = kNegInf;
+    for (int j = 0; j < p.n_split; ++j) {
+        const f32x2 ml = *(const f32x2*)(p.part_ml + 2 * (first + (int64_t)j * QB));
+        if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+    }
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < p.n_split; ++j) {
+        const int64_t r = first + (int64_t)j * QB;
+        const f32x2 ml = *(const f32x2*)(p.part_ml + 2 * r);
+        if (!(ml[1] > 0.f)) continue;
+        const float w = fast_exp2(ml[0] - M);
+        L += w * ml[1];
+        const f32x4 oj = *(const f32x4*)(p.part_o + r * D + 4 * c4);
+        acc += w * oj;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int qtok = p.perm ? p.perm[qpos] : qpos;
+    uint16_t* orow = (uint16_t*)p.out + b * p.o_sb + h * p.o_sh + (int64_t)qtok * p.o_sn;
+    const f32x2 x0 = {acc[0] * inv, acc[1] * inv};
+    const f32x2 x1 = {acc[2] * inv, acc[3] * inv};
+    const uint2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(x0, bf16x2)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(x1, bf16x2))};
+    *(uint2*)(orow + 4 * c4) = w;
+    if (p.lse && c4 == 0)
+        p.lse[(int64_t)bh * p.n_tokens + qtok] =
+            L > 0.f ? (M + __builtin_log2f(L)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -883,10 +955,35 @@ bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block, bool 
     return false;
 }
 
+int na_attn_split_capacity(int dtype, int head_dim, int q_block, bool fusion) {
+    if (dtype != NA_BF16 || fusion) return 0;
+    const void* fn = nullptr;
+    int threads = 0;
+    if (head_dim == 128 && q_block == 384)
+        fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<128, 8>), threads = 512;
+    else if (head_dim == 128 && q_block == 192)
+        fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<128, 4>), threads = 256;
+    else if (head_dim == 64 && q_block == 192)
+        fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<64, 4>), threads = 256;
+    else
+        return 0;
+    int per_cu = 0, dev = -1, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return per_cu > 0 && cus > 0 ? per_cu * cus : 0;
+}
+
 int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, bool fusion,
                    void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    const dim3 grid((unsigned)p.n_wg);
+    // whole tiles, then the shares of the split tail tiles (none without a split)
+    const dim3 grid((unsigned)(p.n_main + (int64_t)(p.n_wg - p.n_main) * p.n_split));
+    const bool split = p.n_main < p.n_wg;
+    const dim3 cgrid((unsigned)(((int64_t)(p.n_wg - p.n_main) * q_block * (head_dim / 4) + 255) / 256));
+    if (split && na_attn_split_capacity(dtype, head_dim, q_block, fusion) == 0)
+        return (int)hipErrorInvalidValue;   // only the 48-query-per-wave kernels run shares
     if (fusion) {
         if (head_dim == 64 && q_block == 64)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 2, true>), grid, dim3(128), 0, st, p);
@@ -909,16 +1006,21 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
             hipLaunchKernelGGL((attn_fwd_bf16<128, 4>), grid, dim3(256), 0, st, p);
         else if (head_dim == 128 && q_block == 256)
             hipLaunchKernelGGL((attn_fwd_bf16<128, 8>), grid, dim3(512), 0, st, p);
-        else if (head_dim == 128 && q_block == 384)
+        else if (head_dim == 128 && q_block == 384) {
             hipLaunchKernelGGL((attn_fwd_bf16_m16<128, 8>), grid, dim3(512), 0, st, p);
+            if (split) hipLaunchKernelGGL((attn_fwd_combine<128, 384>), cgrid, dim3(256), 0, st, p);
+        }
         else if (head_dim == 64 && q_block == 128)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 4>), grid, dim3(256), 0, st, p);
         else if (head_dim == 64 && q_block == 256)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 8>), grid, dim3(512), 0, st, p);
-        else if (head_dim == 128 && q_block == 192)
+        else if (head_dim == 128 && q_block == 192) {
             hipLaunchKernelGGL((attn_fwd_bf16_m16<128, 4>), grid, dim3(256), 0, st, p);
-        else if (head_dim == 64 && q_block == 192)
+            if (split) hipLaunchKernelGGL((attn_fwd_combine<128, 192>), cgrid, dim3(256), 0, st, p);
+        } else if (head_dim == 64 && q_block == 192) {
             hipLaunchKernelGGL((attn_fwd_bf16_m16<64, 4>), grid, dim3(256), 0, st, p);
+            if (split) hipLaunchKernelGGL((attn_fwd_combine<64, 192>), cgrid, dim3(256), 0, st, p);
+        }
         else
             return (int)hipErrorInvalidValue;
     } else {

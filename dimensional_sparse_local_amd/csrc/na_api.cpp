@@ -99,6 +99,25 @@ na_status check_tensor(const na_plan_s* p, const na_tensor* t, const char* name,
     return NA_OK;
 }
 
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Bytes of the permute passes' buffers (gathered q, k, v, out and lse).
+size_t permute_ws_bytes(const na_plan_s* p, int64_t B, int64_t H, uint32_t flags) {
+    if (!(flags & NA_FWD_PERMUTE_PASSES) || p->identity_order) return 0;
+    const size_t rows = (size_t)B * (size_t)H * (size_t)p->n_tokens;
+    const size_t t = rows * (size_t)p->desc.head_dim * (size_t)elem_bytes(p);
+    return 4 * up256(t) + up256(rows * sizeof(float));
+}
+
+// Bytes of the split tail's shares: at most split_capacity of them (one
+// resident round), each q_block rows of head_dim fp32 values plus two floats.
+size_t split_ws_bytes(const na_plan_s* p, uint32_t flags) {
+    if (!(flags & NA_FWD_SPLIT_TAIL) || p->split_capacity <= 0) return 0;
+    const size_t rows = (size_t)p->split_capacity * (size_t)p->desc.q_block;
+    return up256(rows * (size_t)p->desc.head_dim * sizeof(float)) + up256(rows * 2 * sizeof(float));
+}
+
 }  // namespace
 
 void na_set_error(const char* fmt, ...) {
@@ -179,7 +198,12 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
             delete p;
             return st;
         }
+        const na_plan_desc& d = p->desc;
+        p->split_capacity = na_attn_split_capacity(
+            d.dtype, d.head_dim, d.q_block, d.skip > 0 && d.skip_mode == NA_SKIP_FIXED_FUSION);
     }
+    for (size_t t = 0; t + 1 < p->row_ptr.size(); ++t)
+        p->max_row_len = std::max(p->max_row_len, p->row_ptr[t + 1] - p->row_ptr[t]);
     *out = p;
     return NA_OK;
 }
@@ -255,11 +279,7 @@ na_status na_plan_get_order(na_plan_t p, int32_t* host, size_t n) {
 
 size_t na_forward_workspace_bytes(na_plan_t p, int64_t B, int64_t H, uint32_t flags) {
     if (!p || B < 1 || H < 1) return 0;
-    if (!(flags & NA_FWD_PERMUTE_PASSES) || p->identity_order) return 0;
-    const size_t rows = (size_t)B * (size_t)H * (size_t)p->n_tokens;
-    const size_t t = rows * (size_t)p->desc.head_dim * (size_t)elem_bytes(p);
-    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return 4 * up(t) + up(rows * sizeof(float));
+    return permute_ws_bytes(p, B, H, flags) + split_ws_bytes(p, flags);
 }
 
 na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, const na_tensor* k,
@@ -273,7 +293,7 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         na_set_error("plan was built host-only and cannot run");
         return NA_ERR_PLAN_MISMATCH;
     }
-    if (flags & ~NA_FWD_PERMUTE_PASSES) {
+    if (flags & ~(NA_FWD_PERMUTE_PASSES | NA_FWD_SPLIT_TAIL)) {
         na_set_error("unknown forward flags 0x%x", flags);
         return NA_ERR_INVALID_ARG;
     }
@@ -318,11 +338,22 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         return NA_ERR_PLAN_MISMATCH;
     }
     const bool passes = (flags & NA_FWD_PERMUTE_PASSES) && !p->identity_order;
-    if (passes) {
-        const size_t need = na_forward_workspace_bytes(p, B, H, flags);
-        if (!workspace || ws_bytes < need || ((uintptr_t)workspace) % 256 != 0) {
-            na_set_error("permute passes need %zu bytes of 256-byte aligned workspace", need);
-            return NA_ERR_INVALID_ARG;
+    const size_t need = na_forward_workspace_bytes(p, B, H, flags);
+    if (need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace) % 256 != 0)) {
+        na_set_error("forward flags 0x%x need %zu bytes of 256-byte aligned workspace", flags,
+                     need);
+        return NA_ERR_INVALID_ARG;
+    }
+    // split tail: the r query tiles of the last, partly filled round (r at
+    // most half a round) each run as s = capacity / r workgroups over shares
+    // of their walk, so the last round fills the device
+    int64_t n_main = n_wg, n_split = 1;
+    if (split_ws_bytes(p, flags) > 0) {
+        const int64_t cap = p->split_capacity, r = n_wg % cap;
+        const int64_t s = r > 0 ? std::min<int64_t>(cap / r, p->max_row_len) : 0;
+        if (r > 0 && 2 * r <= cap && s >= 2) {
+            n_main = n_wg - r;
+            n_split = s;
         }
     }
 
@@ -331,6 +362,14 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
     a.heads = (int32_t)H;
     a.n_q_tiles = (int32_t)p->stats.n_q_tiles;
     a.n_wg = (int32_t)n_wg;
+    a.n_main = (int32_t)n_main;
+    a.n_split = (int32_t)n_split;
+    if (n_split > 1) {
+        char* sw = (char*)workspace + permute_ws_bytes(p, B, H, flags);
+        const size_t rows = (size_t)p->split_capacity * (size_t)d.q_block;
+        a.part_o = (float*)sw;
+        a.part_ml = (float*)(sw + up256(rows * (size_t)d.head_dim * sizeof(float)));
+    }
     a.scale_log2 = scale * 1.4426950408889634f;
     a.row_ptr = p->d_row_ptr;
     a.entries = p->d_entries;
@@ -371,7 +410,7 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         rc = na_attn_launch(a, d.dtype, d.head_dim, d.q_block, fusion, stream);
     } else {
         // gather q, k, v into sequence order, attend on contiguous tiles, scatter back
-        auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+        auto up = up256;
         const size_t t = (size_t)(B * H * N * D * eb);
         char* ws = (char*)workspace;
         void* qs = ws;

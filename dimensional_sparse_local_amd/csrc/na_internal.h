@@ -69,6 +69,11 @@ struct na_plan_s {
     std::vector<int32_t> p_row_ptr; // ceil(n_kv_tiles / 2) + 1
     std::vector<NaPairEntry> p_entries;
     na_plan_stats stats{};
+    int32_t max_row_len = 0;        // most non-empty key/value tiles of one query tile
+    // workgroups of this plan's forward kernel that fit on the device at once
+    // (compute units x workgroups per unit), for kernels with a split-walk
+    // mode; 0 otherwise or for host-only plans
+    int32_t split_capacity = 0;
 
     // device copies (null when host-only or not needed)
     bool on_device = false;
@@ -123,6 +128,17 @@ struct NaAttnParams {
     // sequence and whether x + pi is fetched too
     int32_t sep_skip;
     int32_t sep_both;
+    // split tail (48-query-per-wave kernels): workgroups below n_main run
+    // whole query tiles (index remapped over n_main); the rest run part
+    // (index - n_main) % n_split of tile n_main + (index - n_main) / n_split:
+    // that share of its walk, writing unnormalised partial results to part_o
+    // ([part][q_block][head_dim] fp32) and part_ml ([part][q_block][2]: the
+    // row's reference maximum (log2 domain) and its row sum), which
+    // attn_fwd_combine merges.  n_main = n_wg and n_split = 1 for no split.
+    int32_t n_main;
+    int32_t n_split;
+    float* part_o;
+    float* part_ml;
 };
 
 // Gradient launch parameters (attn_bwd.hip).  Tensors as in NaAttnParams;
@@ -187,6 +203,10 @@ int na_bwd_scratch(void** ptr, size_t* bytes);
 // fusion = the fixed-fusion (logit bias) variant.
 bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block, bool fusion);
 // Launch the fused attention kernel; returns the HIP error code (0 = success).
+// Workgroups of the forward kernel for (dtype, head_dim, q_block, fusion)
+// resident on the current device at once, if that kernel has the split-walk
+// mode; 0 otherwise.
+int na_attn_split_capacity(int dtype, int head_dim, int q_block, bool fusion);
 int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, bool fusion,
                    void* stream);
 

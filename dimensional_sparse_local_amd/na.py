@@ -21,6 +21,7 @@ NA_BOUND_CLAMP, NA_BOUND_TRUNCATE = 0, 1
 NA_BF16, NA_F32 = 0, 1
 NA_PLAN_HOST_ONLY = 1
 NA_FWD_PERMUTE_PASSES = 1
+NA_FWD_SPLIT_TAIL = 2
 NA_BACKWARD_NOALLOC_MAX_BYTES = 16 << 20
 
 ORDERS = {"row_major": NA_ORDER_ROW_MAJOR, "tiled": NA_ORDER_TILED, "hilbert": NA_ORDER_HILBERT}
@@ -70,7 +71,7 @@ _STATUS = {NA_ERR_INVALID_ARG: "invalid argument", NA_ERR_UNSUPPORTED: "unsuppor
            NA_ERR_PLAN_MISMATCH: "plan mismatch"}
 
 _lib = None
-ABI_VERSION = 5  # NA_ABI_VERSION of include/na.h that Desc mirrors
+ABI_VERSION = 6  # NA_ABI_VERSION of include/na.h that Desc mirrors
 
 
 def lib():
@@ -196,30 +197,33 @@ def desc_from_workload(w: dict, q_block: int = 0, kv_block: int = 0) -> Desc:
     return d
 
 
-def forward_launch(w: dict) -> tuple[dict, int]:
-    """(kernel-side workload, query tile) for the forward pass alone, the
-    fastest measured launch of each shape:
+def forward_launch(w: dict) -> tuple[dict, int, bool]:
+    """(kernel-side workload, query tile, split tail) for the forward pass
+    alone, the fastest measured launch of each shape:
 
     * bf16, head_dim 128, no fixed-fusion bias: 384-query tiles (the 16x16x32
       MFMA kernel, 48 queries per wave): each staged K/V tile serves 1.5x the
-      queries of a 256-query tile, on full and partial tile pairs alike;
+      queries of a 256-query tile, on full and partial tile pairs alike; with
+      the split tail, so that a last round of workgroups that would leave
+      most compute units idle is spread over all of them;
     * bf16, head_dim 64, 2-D neighbourhood or slide window in row-major order:
       8x8 patch order inside the kernel (q, k, v, out stay row-major) makes the
       visited tile pairs denser, and 64-query tiles give the short walks more
       workgroups;
-    * otherwise the library defaults (the workload as given, query tile 0).
+    * otherwise the library defaults (the workload as given, query tile 0,
+      no split).
 
     The gradient kernels take 128- or 256-query tiles: a plan made for the
     backward pass keeps the defaults."""
     pat = w["pattern"]
     bias = pat.get("skip", 0) > 0 and pat.get("skip_mode", "union") == "fixed_fusion"
     if w.get("dtype", "bf16") == "bf16" and int(w["D"]) == 128 and not bias:
-        return w, 384
+        return w, 384, True
     if (w.get("dtype", "bf16") == "bf16" and int(w["D"]) == 64
             and w.get("order", "row_major") == "row_major" and len(w["grid"]) == 2
             and pat["kind"] in ("na", "sa")):
-        return dict(w, order="tiled", tile=[8, 8]), 64
-    return w, 0
+        return dict(w, order="tiled", tile=[8, 8]), 64, False
+    return w, 0, False
 
 
 class Plan:
@@ -302,8 +306,10 @@ class Plan:
         return Tensor(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
 
     def forward(self, q, k, v, out=None, lse=True, scale=None, permute_passes=False,
-                workspace=None, stream=None):
-        """(out, lse) for [B, H, N, D] tensors in row-major token order."""
+                split_tail=False, workspace=None, stream=None):
+        """(out, lse) for [B, H, N, D] tensors in row-major token order.
+        split_tail: NA_FWD_SPLIT_TAIL (the last round's query tiles split over
+        the idle compute units; 48-query-per-wave kernels only)."""
         import torch
 
         B, H = int(q.shape[0]), int(q.shape[1])
@@ -321,7 +327,8 @@ class Plan:
             raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
         if scale is None:
             scale = 1.0 / math.sqrt(self.head_dim)
-        flags = NA_FWD_PERMUTE_PASSES if permute_passes else 0
+        flags = ((NA_FWD_PERMUTE_PASSES if permute_passes else 0)
+                 | (NA_FWD_SPLIT_TAIL if split_tail else 0))
         ws_bytes = int(lib().na_forward_workspace_bytes(self._h, B, H, flags))
         if ws_bytes and workspace is None:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)

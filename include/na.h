@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define NA_ABI_VERSION 5
+#define NA_ABI_VERSION 6
 
 typedef enum {
     NA_OK = 0,
@@ -105,6 +105,16 @@ enum { NA_BF16 = 0, NA_F32 = 1 };
                                     the permute kernel, attend on contiguous tiles, scatter out and
                                     lse back (needs na_forward_workspace_bytes of workspace). Default:
                                     the attention kernel gathers and scatters rows itself. */
+#define NA_FWD_SPLIT_TAIL 2u /* for the 48-query-per-wave kernels (bf16, q_block 192 or 384, no
+                                fixed fusion): when the query tiles of the last round of
+                                workgroups fill at most half of the GPU, each of those r tiles
+                                runs as s = (resident workgroups) / r workgroups, each over one
+                                contiguous share of the tile's key/value walk, writing
+                                unnormalised partial results (fp32) that a second kernel merges;
+                                the last round then fills the GPU.  Smaller problems (fewer tiles
+                                than half a round) split every tile.  Needs
+                                na_forward_workspace_bytes of workspace (at most one round of
+                                shares, independent of B and H); no effect on other kernels. */
 
 /*
  * Plan descriptor.  Pattern dimensions are the grid dimensions, except for
@@ -224,7 +234,9 @@ na_status na_plan_get_classes(na_plan_t plan, uint8_t* host_classes, size_t n);
 na_status na_plan_get_order(na_plan_t plan, int32_t* host_perm, size_t n);
 
 /* Workspace bytes na_forward needs for (B, H) with the given flags (0 for the
- * default fused path). */
+ * default fused path): the permute passes' gathered q, k, v, out and lse,
+ * then the split tail's shares (resident workgroups x q_block x (head_dim + 2)
+ * fp32 values), each part rounded up to 256 bytes. */
 size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t flags);
 
 /* out = softmax attention of q over its neighbourhood keys/values, lse as
@@ -232,8 +244,9 @@ size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t
  * z_ij = scale q_i . k_j ("pi-Attention", Section 3.1, Eqs. 1-3, restricted
  * to the neighbourhood as in Section 3.2, Eqs. 4-5).  q, k, v, out are
  * caller-owned device tensors and lse a caller-owned device buffer; nothing is
- * allocated (the permute-passes path uses the caller's workspace, >=
- * na_forward_workspace_bytes, 256-byte aligned).  q, k, v, out share the
+ * allocated (the permute passes and the split tail use the caller's
+ * workspace, >= na_forward_workspace_bytes, 256-byte aligned).  Flags: 0,
+ * NA_FWD_PERMUTE_PASSES, NA_FWD_SPLIT_TAIL or both.  q, k, v, out share the
  * plan's dtype and head_dim; lse may be NULL;
  * scale must be finite and positive (NA_ERR_INVALID_ARG otherwise).
  * Returns NA_ERR_PLAN_MISMATCH if the plan was built host-only, and

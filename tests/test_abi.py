@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = na.lib()
-    assert lib.na_abi_version() == na.ABI_VERSION == 5
+    assert lib.na_abi_version() == na.ABI_VERSION == 6
     for s in range(6):
         assert lib.na_status_string(s)
     assert lib.na_status_string(99) == b"unknown status"
@@ -148,3 +148,16 @@ def test_backward_noalloc_refuses_before_device_work():
     st = L.na_backward_noalloc(big._h, 1, 3, *([None] * 9), 0.1, None)   # fits: 3 * N rows
     assert st == na.NA_ERR_PLAN_MISMATCH
     assert L.na_backward_noalloc(big._h, 0, 3, *([None] * 9), 0.1, None) == na.NA_ERR_INVALID_ARG
+
+
+def test_split_tail_flag_on_host_only_plan():
+    """A host-only plan has no device to size a round of workgroups for: the
+    split tail needs no workspace there, and unknown forward flags are
+    refused."""
+    L = na.lib()
+    plan = na.Plan(W.scaled(W.CONFIGS["causal1d_bf16"], H=2, grid=[3000],
+                            pattern=dict(kind="band", left=600, right=0)),
+                   host_only=True, q_block=384)
+    assert int(L.na_forward_workspace_bytes(plan._h, 1, 2, na.NA_FWD_SPLIT_TAIL)) == 0
+    st = L.na_forward(plan._h, 1, 2, None, None, None, None, None, 0.1, 4, None, 0, None)
+    assert st in (na.NA_ERR_INVALID_ARG, na.NA_ERR_PLAN_MISMATCH)

@@ -56,14 +56,16 @@ def _check(wl, out, lse, ref_out, ref_lse, rows=None, label=""):
     return err
 
 
-def _run(wl, rows=None, q_block=0, permute_passes=False, seed=None):
+def _run(wl, rows=None, q_block=0, permute_passes=False, seed=None, split_tail=False):
     na = _na()
-    print("case %s grid=%s B=%d H=%d D=%d q_block=%d passes=%s" % (
-        wl["name"], wl["grid"], wl["B"], wl["H"], wl["D"], q_block, permute_passes), flush=True)
+    print("case %s grid=%s B=%d H=%d D=%d q_block=%d passes=%s split=%s" % (
+        wl["name"], wl["grid"], wl["B"], wl["H"], wl["D"], q_block, permute_passes, split_tail),
+        flush=True)
     plan = na.Plan(wl, q_block=q_block)
     q, k, v = W.make_qkv(wl, device="cuda", seed=seed)
     scale = W.default_scale(wl)
-    out, lse = plan.forward(q, k, v, scale=scale, permute_passes=permute_passes)
+    out, lse = plan.forward(q, k, v, scale=scale, permute_passes=permute_passes,
+                            split_tail=split_tail)
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.attention(wl, q.cpu(), k.cpu(), v.cpu(), scale, rows=rows)
     return _check(wl, out, lse, ref_out, ref_lse, rows=rows, label=wl["name"])
@@ -158,6 +160,46 @@ def test_d128_q384(wl):
     """Eight waves of 48 queries (three 16-query MFMA blocks each) on the same
     cases."""
     _run(wl, q_block=384)
+
+
+# The split tail (NA_FWD_SPLIT_TAIL).  With fewer query tiles than half a
+# round of resident workgroups every tile's walk is split (into up to its
+# length shares, so some shares are empty); the 33-head band has one round of
+# whole tiles plus a tail of 8 split ones (at 256 resident workgroups).
+SPLIT = ([(w, 384) for w in D128_QB256] + [(w, 192) for w in SMALL_BF16]
+         + [(W.scaled(W.CONFIGS["causal1d_bf16"], name="band_tail_h33", H=33, grid=[3000],
+                      pattern=dict(kind="band", left=600, right=0)), 384),
+            (W.scaled(W.CONFIGS["sta3d_bf16"], name="sta_tail_h9", H=9, grid=[12, 16, 40],
+                      pattern=dict(kind="sta", tile=[6, 8, 8], window_tiles=[1, 2, 3])), 384)])
+
+
+@pytest.mark.parametrize("wl,q_block", SPLIT, ids=["%s-%d" % (w["name"], qb) for w, qb in SPLIT])
+def test_split_tail(wl, q_block):
+    _run(wl, q_block=q_block, split_tail=True)
+
+
+def test_split_tail_workspace_and_permute_passes():
+    """The workspace holds at most one round of shares, whatever B and H, after
+    the permute passes' buffers when both flags are given; both together give
+    the oracle's result."""
+    na = _na()
+    wl = W.scaled(W.CONFIGS["hilbert_band_bf16"], name="d128_hilbert_split", B=1, H=2, D=128,
+                  grid=[32, 32], pattern=dict(kind="band", left=100, right=100))
+    plan = na.Plan(wl, q_block=384)
+    L = na.lib()
+    one = int(L.na_forward_workspace_bytes(plan._h, 1, 1, na.NA_FWD_SPLIT_TAIL))
+    assert one > 0 and one == int(L.na_forward_workspace_bytes(plan._h, 7, 9,
+                                                                na.NA_FWD_SPLIT_TAIL))
+    assert one % 256 == 0
+    perm = int(L.na_forward_workspace_bytes(plan._h, 1, 2, na.NA_FWD_PERMUTE_PASSES))
+    both = int(L.na_forward_workspace_bytes(plan._h, 1, 2,
+                                            na.NA_FWD_PERMUTE_PASSES | na.NA_FWD_SPLIT_TAIL))
+    assert both == perm + one
+    # no split mode at 256-query tiles: the flag costs nothing there
+    plan256 = na.Plan(wl, q_block=256)
+    assert int(L.na_forward_workspace_bytes(plan256._h, 1, 2, na.NA_FWD_SPLIT_TAIL)) == 0
+    _run(wl, q_block=384, permute_passes=True, split_tail=True)
+    _run(wl, q_block=256, split_tail=True)
 
 
 def test_hilbert_permute_passes():
@@ -275,13 +317,13 @@ def test_abi_rejects_bad_tensors():
 
 def _launched(wl):
     na = _na()
-    kwl, q_block = na.forward_launch(wl)
-    print("case %s launched as order=%s q_block=%d" % (wl["name"], kwl["order"], q_block),
-          flush=True)
+    kwl, q_block, split = na.forward_launch(wl)
+    print("case %s launched as order=%s q_block=%d split_tail=%s" % (
+        wl["name"], kwl["order"], q_block, split), flush=True)
     plan = na.Plan(kwl, q_block=q_block)
     q, k, v = W.make_qkv(wl, device="cuda")
     scale = W.default_scale(wl)
-    out, lse = plan.forward(q, k, v, scale=scale)
+    out, lse = plan.forward(q, k, v, scale=scale, split_tail=split)
     torch.cuda.synchronize()
     return plan, q, k, v, scale, out, lse
 
