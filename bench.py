@@ -32,17 +32,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def read_traffic(kernel_sig: str, workload: str, q_block: int):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
-    was taken on the current kernel source, this workload and query tile (null
-    otherwise)."""
+def read_traffic(kernel_sig: str, workload: str, q_block: int, split_tail: bool, passes: bool):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 PMC summary, if it was taken on the current kernel source, this
+    workload, query tile and launch flags (null otherwise)."""
     try:
         with open(PROFILE_PMC) as f:
             for line in f:
                 if line.startswith("traffic_json:"):
                     d = json.loads(line.split(":", 1)[1])
                     if (d.get("kernel_sig") == kernel_sig and d.get("workload") == workload
-                            and d.get("q_block", 256) == q_block):
+                            and d.get("q_block", 256) == q_block
+                            and bool(d.get("split_tail", False)) == split_tail
+                            and bool(d.get("permute_passes", False)) == passes):
                         return d.get("bytes_per_launch")
     except OSError:
         pass
@@ -327,7 +329,8 @@ def main():
     else:
         metric = "effective TFLOP/s (unmasked FLOPs), %s%s" % (
             wl.get("note", name), ", backward pass" if args.which == "backward" else "")
-    traffic = read_traffic(sig, name, plan.stats["q_block"]) if args.which == "forward" else None
+    traffic = (read_traffic(sig, name, plan.stats["q_block"], split, bool(args.permute_passes))
+               if args.which == "forward" else None)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}

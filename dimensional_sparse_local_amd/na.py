@@ -47,7 +47,7 @@ class Desc(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "n_tokens", "q_block", "kv_block", "n_q_tiles", "n_kv_tiles", "n_empty", "n_partial",
-        "n_full", "attended_pairs")]
+        "n_full", "attended_pairs", "resident_workgroups")]
 
 
 class Bounds(ctypes.Structure):
@@ -71,7 +71,7 @@ _STATUS = {NA_ERR_INVALID_ARG: "invalid argument", NA_ERR_UNSUPPORTED: "unsuppor
            NA_ERR_PLAN_MISMATCH: "plan mismatch"}
 
 _lib = None
-ABI_VERSION = 6  # NA_ABI_VERSION of include/na.h that Desc mirrors
+ABI_VERSION = 7  # NA_ABI_VERSION of include/na.h that Desc mirrors
 
 
 def lib():

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define NA_ABI_VERSION 6
+#define NA_ABI_VERSION 7
 
 typedef enum {
     NA_OK = 0,
@@ -106,14 +106,16 @@ enum { NA_BF16 = 0, NA_F32 = 1 };
                                     lse back (needs na_forward_workspace_bytes of workspace). Default:
                                     the attention kernel gathers and scatters rows itself. */
 #define NA_FWD_SPLIT_TAIL 2u /* for the 48-query-per-wave kernels (bf16, q_block 192 or 384, no
-                                fixed fusion): when the query tiles of the last round of
-                                workgroups fill at most half of the GPU, each of those r tiles
-                                runs as s = (resident workgroups) / r workgroups, each over one
-                                contiguous share of the tile's key/value walk, writing
-                                unnormalised partial results (fp32) that a second kernel merges;
-                                the last round then fills the GPU.  Smaller problems (fewer tiles
-                                than half a round) split every tile.  Needs
-                                na_forward_workspace_bytes of workspace (at most one round of
+                                fixed fusion): the r query tiles of the last, partly filled round
+                                of workgroups (r = tiles mod resident_workgroups of the plan's
+                                stats) each run as s workgroups, each over one contiguous share of
+                                the tile's key/value walk, writing unnormalised partial results
+                                (fp32) that a second kernel merges.  s (2 to 16, r s at most four
+                                rounds) minimises ceil(r s / resident) / s, the length of the
+                                shares' rounds in whole-tile rounds; no split unless that is at
+                                most 1/2 (each share pays its own Q load and pipeline fill).
+                                Smaller problems (fewer tiles than one round) split every tile.
+                                Needs na_forward_workspace_bytes of workspace (four rounds of
                                 shares, independent of B and H); no effect on other kernels. */
 
 /*
@@ -170,6 +172,10 @@ typedef struct {
     int64_t attended_pairs;             /* sum over queries of |neighbourhood|, per (batch, head);
                                            with a skip partner |window u partners|, or
                                            |window| + |partners| for NA_SKIP_SEPARATE */
+    int64_t resident_workgroups;        /* workgroups of the plan's forward kernel resident on its
+                                           device at once (compute units x workgroups per unit),
+                                           the round NA_FWD_SPLIT_TAIL balances; 0 for host-only
+                                           plans and kernels without that mode */
 } na_plan_stats;
 
 /* Speedup bounds of a pattern over dense attention of the same length and
@@ -235,8 +241,8 @@ na_status na_plan_get_order(na_plan_t plan, int32_t* host_perm, size_t n);
 
 /* Workspace bytes na_forward needs for (B, H) with the given flags (0 for the
  * default fused path): the permute passes' gathered q, k, v, out and lse,
- * then the split tail's shares (resident workgroups x q_block x (head_dim + 2)
- * fp32 values), each part rounded up to 256 bytes. */
+ * then the split tail's shares (4 x resident workgroups x q_block x
+ * (head_dim + 2) fp32 values), each part rounded up to 256 bytes. */
 size_t na_forward_workspace_bytes(na_plan_t plan, int64_t B, int64_t H, uint32_t flags);
 
 /* out = softmax attention of q over its neighbourhood keys/values, lse as

@@ -163,13 +163,14 @@ def test_d128_q384(wl):
 
 
 # The split tail (NA_FWD_SPLIT_TAIL).  With fewer query tiles than half a
-# round of resident workgroups every tile's walk is split (into up to its
-# length shares, so some shares are empty); the 33-head band has one round of
-# whole tiles plus a tail of 8 split ones (at 256 resident workgroups).
+# round of resident workgroups every tile's walk is split (into up to 16
+# shares, or its length, so some shares may be empty); at 256 resident
+# workgroups the 33-head band (264 tiles) and the 14-head sliding tiles (280)
+# have one round of whole tiles plus a split tail of 8 and 24 tiles.
 SPLIT = ([(w, 384) for w in D128_QB256] + [(w, 192) for w in SMALL_BF16]
          + [(W.scaled(W.CONFIGS["causal1d_bf16"], name="band_tail_h33", H=33, grid=[3000],
                       pattern=dict(kind="band", left=600, right=0)), 384),
-            (W.scaled(W.CONFIGS["sta3d_bf16"], name="sta_tail_h9", H=9, grid=[12, 16, 40],
+            (W.scaled(W.CONFIGS["sta3d_bf16"], name="sta_tail_h14", H=14, grid=[12, 16, 40],
                       pattern=dict(kind="sta", tile=[6, 8, 8], window_tiles=[1, 2, 3])), 384)])
 
 
