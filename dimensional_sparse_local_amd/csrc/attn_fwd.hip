@@ -224,15 +224,31 @@ void attn_fwd_bf16(NaAttnParams p) {
     };
     // s <- 2^(c s - m_ref), fp32; returns this lane's sum of them.  A row with
     // no reference yet (m_ref = -inf) takes 0 here and is redone below.
-    auto probs = [&](f32x16* s) {
+    auto probs = [&](f32x16* s, uint32_t live) {
         const float neg_m = m_ref == kNegInf ? 0.f : -m_ref;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+            if ((live >> kb) & 1u) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+                for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            }
+        }
         return tile_sum32(s[0], s[1]);
     };
+    // On a partial tile a 32-key block that no query of this wave attends
+    // skips its exponentials and P.V products, and the wave skips the whole
+    // tile when both are.
     auto compute = [&](NaEntry entry, const u32x2 (*ml)[QB], const uint16_t* kl, const uint16_t* vl) {
+        uint32_t live = 3u;
+        if (entry.mask >= 0) {
+            const u32x2 any = ml[0][mrow];   // the keep plane holds every attended key
+            live = (__builtin_amdgcn_ballot_w64(any[0] != 0u) ? 1u : 0u) |
+                   (__builtin_amdgcn_ballot_w64(any[1] != 0u) ? 2u : 0u);
+            if (live == 0u) return;
+        }
         f32x16 s[2];
         scores(entry, ml, kl, s);
         // Online softmax against a reference maximum that moves only when it
@@ -243,7 +259,7 @@ void attn_fwd_bf16(NaAttnParams p) {
         // scores and moves every row's reference to max(reference, tile
         // maximum), rescaling O and l; the result is exact after the final
         // division by l either way.
-        float ts = probs(s);
+        float ts = probs(s, live);
         const bool redo = m_ref == kNegInf || !(ts <= kSumMax);
         if (__builtin_amdgcn_ballot_w64(redo)) {
             scores(entry, ml, kl, s);
@@ -262,7 +278,7 @@ void attn_fwd_bf16(NaAttnParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
             }
-            ts = probs(s);
+            ts = probs(s, live);
         }
         // the row sum takes the fp32 probabilities, before their rounding to
         // bf16 for P V, so lse carries fp32 rounding only
@@ -273,6 +289,7 @@ void attn_fwd_bf16(NaAttnParams p) {
         // deliver for that slot.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            if (!((live >> (ks / 2)) & 1u)) continue;
             const f32x16& sv = s[ks / 2];
             const int r0 = 8 * (ks % 2);
             const bf16x8 bp = cvt8(sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
