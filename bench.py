@@ -60,12 +60,21 @@ def _stats(xs):
 
 
 def kernel_signature() -> str:
+    """sha256[:16] of the source of the 48-query-per-wave forward kernel and
+    its combine kernel (the part of attn_fwd.hip from the 16x16x32 helpers to
+    the fp32 kernel) followed by attn_common.h: the code the committed
+    traffic counters were taken on."""
     import hashlib
 
+    csrc = os.path.join(ROOT, "dimensional_sparse_local_amd", "csrc")
+    with open(os.path.join(csrc, "attn_fwd.hip"), "rb") as f:
+        text = f.read()
+    start = text.index(b"__device__ __forceinline__ float quad_max(float x) {")
+    end = text.index(b"// fp32: one wave, 32 queries", start)
     h = hashlib.sha256()
-    for name in ("attn_fwd.hip", "attn_common.h"):
-        with open(os.path.join(ROOT, "dimensional_sparse_local_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    h.update(text[start:end])
+    with open(os.path.join(csrc, "attn_common.h"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
