@@ -262,6 +262,36 @@ def test_strided_views_and_poison():
     assert not torch.isnan(out).any()
 
 
+@pytest.mark.parametrize("q_block", [256, 384])
+def test_nan_input_contract(q_block):
+    """The stated contract for non-finite inputs: a NaN or infinity in k or v
+    leaves out and lse unspecified only for queries whose query tile visits
+    the key tile that holds it; every other query's out and lse are bit for
+    bit those of the clean inputs (and the launch completes normally)."""
+    na = _na()
+    wl = W.scaled(W.CONFIGS["causal1d_bf16"], name="nan_contract", H=2, grid=[3000],
+                  pattern=dict(kind="band", left=200, right=0))
+    plan = na.Plan(wl, q_block=q_block)
+    q, k, v = W.make_qkv(wl, device="cuda")
+    ref, ref_lse = plan.forward(q, k, v, scale=0.1)
+    bad_tok = 1500
+    kn, vn = k.clone(), v.clone()
+    kn[:, :, bad_tok, 3] = float("nan")
+    vn[:, :, bad_tok, 5] = float("inf")
+    out, lse = plan.forward(q, kn, vn, scale=0.1)
+    torch.cuda.synchronize()
+    cls = plan.classes()
+    kt = bad_tok // plan.stats["kv_block"]
+    qb = plan.stats["q_block"]
+    clean = np.ones(plan.n_tokens, dtype=bool)
+    for t in np.nonzero(cls[:, kt])[0]:
+        clean[t * qb:(t + 1) * qb] = False
+    assert clean.any() and not clean.all()
+    idx = torch.from_numpy(np.nonzero(clean)[0]).cuda()
+    assert torch.equal(out[:, :, idx], ref[:, :, idx])
+    assert torch.equal(lse[:, :, idx], ref_lse[:, :, idx])
+
+
 def test_deterministic():
     na = _na()
     wl = W.scaled(W.CONFIGS["hilbert_band_bf16"], name="det", B=1, H=2, grid=[32, 32],
