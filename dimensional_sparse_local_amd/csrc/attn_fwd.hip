@@ -76,7 +76,11 @@ void attn_fwd_bf16(NaAttnParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     const int half = lane >> 5, l32 = lane & 31;
 
-    const int wg = xcd_remap(blockIdx.x, p.n_wg);
+    // whole tile, or one share of a tail tile's walk (split tail; never with
+    // the fixed-fusion bias or the fused partner branch)
+    const bool part_mode = (int)blockIdx.x >= p.n_main;
+    const int part = (int)blockIdx.x - p.n_main;
+    const int wg = part_mode ? p.n_main + part / p.n_split : xcd_remap(blockIdx.x, p.n_main);
     const int qt = wg % p.n_q_tiles;
     const int bh = wg / p.n_q_tiles;
     const int b = bh / p.heads, h = bh % p.heads;
@@ -309,7 +313,12 @@ void attn_fwd_bf16(NaAttnParams p) {
     // Entering step e: tile e (K, V and its mask rows) is in flight to (or in)
     // its LDS buffers, ent_a..c are the entries of tiles e..e+2 and tok_n the
     // tokens of tile e+1.
-    const int e0 = cload(p.row_ptr + qt), e1 = cload(p.row_ptr + qt + 1);
+    int e0 = cload(p.row_ptr + qt), e1 = cload(p.row_ptr + qt + 1);
+    if (part_mode) {
+        const int len = e1 - e0, j = part % p.n_split;
+        e1 = e0 + (len * (j + 1)) / p.n_split;
+        e0 = e0 + (len * j) / p.n_split;
+    }
     const NaEntry none = {0, -1};
     NaEntry ent_a = none, ent_b = none, ent_c = none;
     int tok_n[IPW];
@@ -340,10 +349,14 @@ void attn_fwd_bf16(NaAttnParams p) {
     }
 
     // ---- epilogue -----------------------------------------------------------
+    // A share of a split tile stores its unnormalised O (fp32), reference
+    // maximum and row sum for the merge; a whole tile stores O / l and lse.
     const float l_tot = halves_sum(l_run);
-    if (!qvalid) return;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const bool share = !BIAS && part_mode;
+    if (!share && !qvalid) return;
+    const float inv = share ? 1.f : (l_tot > 0.f ? 1.f / l_tot : 0.f);
     uint16_t* orow = (uint16_t*)p.out + b * p.o_sb + h * p.o_sh + (int64_t)qtok * p.o_sn;
+    const int64_t srow = (int64_t)part * QB + wave * 32 + l32;   // share mode: row of part_o
     // pi-Attention's separate softmax ("pi-Attention", Section 3.5, Eq. 15):
     // the softmax over this query's online partners x - pi (and x + pi; Eq. 9),
     // a separate distribution whose weighted value average is added to the
@@ -444,12 +457,20 @@ void attn_fwd_bf16(NaAttnParams p) {
                     }
                 }
             }
+            if (share) {
+                *(f32x4*)(p.part_o + srow * D + d) = f32x4{y[0], y[1], y[2], y[3]};
+                continue;
+            }
             const f32x2 x0 = {y[0], y[1]};
             const f32x2 x1 = {y[2], y[3]};
             const uint2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(x0, bf16x2)),
                              __builtin_bit_cast(uint32_t, __builtin_convertvector(x1, bf16x2))};
             *(uint2*)(orow + d) = w;
         }
+    if (share) {
+        if (half == 0) *(f32x2*)(p.part_ml + 2 * srow) = f32x2{m_ref, l_tot};
+        return;
+    }
     if (p.lse && half == 0) {
         float lse = l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
         if constexpr (BIAS) lse += p.lse_shift;  // the log(alpha) common to every logit
@@ -976,7 +997,17 @@ int na_attn_split_capacity(int dtype, int head_dim, int q_block, bool fusion) {
     if (dtype != NA_BF16 || fusion) return 0;
     const void* fn = nullptr;
     int threads = 0;
-    if (head_dim == 128 && q_block == 384)
+    if (head_dim == 64 && q_block == 64)
+        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 2>), threads = 128;
+    else if (head_dim == 64 && q_block == 128)
+        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 4>), threads = 256;
+    else if (head_dim == 64 && q_block == 256)
+        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 8>), threads = 512;
+    else if (head_dim == 128 && q_block == 128)
+        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<128, 4>), threads = 256;
+    else if (head_dim == 128 && q_block == 256)
+        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<128, 8>), threads = 512;
+    else if (head_dim == 128 && q_block == 384)
         fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<128, 8>), threads = 512;
     else if (head_dim == 128 && q_block == 192)
         fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<128, 4>), threads = 256;
@@ -999,8 +1030,8 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
     const dim3 grid((unsigned)(p.n_main + (int64_t)(p.n_wg - p.n_main) * p.n_split));
     const bool split = p.n_main < p.n_wg;
     const dim3 cgrid((unsigned)(((int64_t)(p.n_wg - p.n_main) * q_block * (head_dim / 4) + 255) / 256));
-    if (split && na_attn_split_capacity(dtype, head_dim, q_block, fusion) == 0)
-        return (int)hipErrorInvalidValue;   // only the 48-query-per-wave kernels run shares
+    if (split && (na_attn_split_capacity(dtype, head_dim, q_block, fusion) == 0 || p.sep_skip > 0))
+        return (int)hipErrorInvalidValue;   // no shares with the bias or the fused partner branch
     if (fusion) {
         if (head_dim == 64 && q_block == 64)
             hipLaunchKernelGGL((attn_fwd_bf16<64, 2, true>), grid, dim3(128), 0, st, p);
@@ -1017,20 +1048,27 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
         return (int)hipGetLastError();
     }
     if (dtype == NA_BF16) {
-        if (head_dim == 64 && q_block == 64)
+        if (head_dim == 64 && q_block == 64) {
             hipLaunchKernelGGL((attn_fwd_bf16<64, 2>), grid, dim3(128), 0, st, p);
-        else if (head_dim == 128 && q_block == 128)
+            if (split) hipLaunchKernelGGL((attn_fwd_combine<64, 64>), cgrid, dim3(256), 0, st, p);
+        } else if (head_dim == 128 && q_block == 128) {
             hipLaunchKernelGGL((attn_fwd_bf16<128, 4>), grid, dim3(256), 0, st, p);
-        else if (head_dim == 128 && q_block == 256)
+            if (split) hipLaunchKernelGGL((attn_fwd_combine<128, 128>), cgrid, dim3(256), 0, st, p);
+        } else if (head_dim == 128 && q_block == 256) {
             hipLaunchKernelGGL((attn_fwd_bf16<128, 8>), grid, dim3(512), 0, st, p);
+            if (split) hipLaunchKernelGGL((attn_fwd_combine<128, 256>), cgrid, dim3(256), 0, st, p);
+        }
         else if (head_dim == 128 && q_block == 384) {
             hipLaunchKernelGGL((attn_fwd_bf16_m16<128, 8>), grid, dim3(512), 0, st, p);
             if (split) hipLaunchKernelGGL((attn_fwd_combine<128, 384>), cgrid, dim3(256), 0, st, p);
         }
-        else if (head_dim == 64 && q_block == 128)
+        else if (head_dim == 64 && q_block == 128) {
             hipLaunchKernelGGL((attn_fwd_bf16<64, 4>), grid, dim3(256), 0, st, p);
-        else if (head_dim == 64 && q_block == 256)
+            if (split) hipLaunchKernelGGL((attn_fwd_combine<64, 128>), cgrid, dim3(256), 0, st, p);
+        } else if (head_dim == 64 && q_block == 256) {
             hipLaunchKernelGGL((attn_fwd_bf16<64, 8>), grid, dim3(512), 0, st, p);
+            if (split) hipLaunchKernelGGL((attn_fwd_combine<64, 256>), cgrid, dim3(256), 0, st, p);
+        }
         else if (head_dim == 128 && q_block == 192) {
             hipLaunchKernelGGL((attn_fwd_bf16_m16<128, 4>), grid, dim3(256), 0, st, p);
             if (split) hipLaunchKernelGGL((attn_fwd_combine<128, 192>), cgrid, dim3(256), 0, st, p);

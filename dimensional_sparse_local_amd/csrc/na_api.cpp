@@ -203,8 +203,14 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
             delete p;
             return st;
         }
+        // the split tail runs on the bf16 kernels without the fixed-fusion
+        // bias and without the separate softmax's partner branch in their
+        // epilogue (the 32-query-per-wave kernels fuse it; at q_block 192 and
+        // 384 it is a second kernel after the merge)
         const na_plan_desc& d = p->desc;
-        p->split_capacity = na_attn_split_capacity(
+        const bool sep_in_epilogue = d.skip > 0 && d.skip_mode == NA_SKIP_SEPARATE &&
+                                     d.q_block != 192 && d.q_block != 384;
+        p->split_capacity = sep_in_epilogue ? 0 : na_attn_split_capacity(
             d.dtype, d.head_dim, d.q_block, d.skip > 0 && d.skip_mode == NA_SKIP_FIXED_FUSION);
         p->stats.resident_workgroups = p->split_capacity;
     }

@@ -211,7 +211,9 @@ def forward_launch(w: dict) -> tuple[dict, int, bool]:
       visited tile pairs denser, and 64-query tiles give the short walks more
       workgroups;
     * otherwise the library defaults (the workload as given, query tile 0,
-      no split).
+      no split: on the short, latency-bound walks of the head_dim-64
+      workloads the merge kernel's launch costs more than a split tail saves,
+      e.g. 47 -> 56 us on the 96x96 shifted Hilbert windows).
 
     The gradient kernels take 128- or 256-query tiles: a plan made for the
     backward pass keeps the defaults."""

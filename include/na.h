@@ -105,8 +105,10 @@ enum { NA_BF16 = 0, NA_F32 = 1 };
                                     the permute kernel, attend on contiguous tiles, scatter out and
                                     lse back (needs na_forward_workspace_bytes of workspace). Default:
                                     the attention kernel gathers and scatters rows itself. */
-#define NA_FWD_SPLIT_TAIL 2u /* for the 48-query-per-wave kernels (bf16, q_block 192 or 384, no
-                                fixed fusion): the r query tiles of the last, partly filled round
+#define NA_FWD_SPLIT_TAIL 2u /* for the bf16 kernels without fixed fusion (and, at q_block 64,
+                                128 or 256, without the separate softmax, whose partner branch
+                                those kernels add in their epilogue): the r query tiles of the
+                                last, partly filled round
                                 of workgroups (r = tiles mod resident_workgroups of the plan's
                                 stats) each run as s workgroups, each over one contiguous share of
                                 the tile's key/value walk, writing unnormalised partial results
@@ -116,7 +118,7 @@ enum { NA_BF16 = 0, NA_F32 = 1 };
                                 most 1/2 (each share pays its own Q load and pipeline fill).
                                 Smaller problems (fewer tiles than one round) split every tile.
                                 Needs na_forward_workspace_bytes of workspace (four rounds of
-                                shares, independent of B and H); no effect on other kernels. */
+                                shares, independent of B and H); no effect on other launches. */
 
 /*
  * Plan descriptor.  Pattern dimensions are the grid dimensions, except for

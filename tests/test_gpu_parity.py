@@ -167,7 +167,9 @@ def test_d128_q384(wl):
 # shares, or its length, so some shares may be empty); at 256 resident
 # workgroups the 33-head band (264 tiles) and the 14-head sliding tiles (280)
 # have one round of whole tiles plus a split tail of 8 and 24 tiles.
-SPLIT = ([(w, 384) for w in D128_QB256] + [(w, 192) for w in SMALL_BF16]
+SPLIT = ([(w, 384) for w in D128_QB256] + [(w, 256) for w in D128_QB256]
+         + [(w, 192) for w in SMALL_BF16] + [(w, 128) for w in SMALL_BF16]
+         + [(w, 64) for w in SMALL_BF16 if w["D"] == 64]
          + [(W.scaled(W.CONFIGS["causal1d_bf16"], name="band_tail_h33", H=33, grid=[3000],
                       pattern=dict(kind="band", left=600, right=0)), 384),
             (W.scaled(W.CONFIGS["sta3d_bf16"], name="sta_tail_h14", H=14, grid=[12, 16, 40],
@@ -177,6 +179,14 @@ SPLIT = ([(w, 384) for w in D128_QB256] + [(w, 192) for w in SMALL_BF16]
 @pytest.mark.parametrize("wl,q_block", SPLIT, ids=["%s-%d" % (w["name"], qb) for w, qb in SPLIT])
 def test_split_tail(wl, q_block):
     _run(wl, q_block=q_block, split_tail=True)
+
+
+@pytest.mark.parametrize("name", ["hwa96_bf16", "hna96_bf16"])
+def test_split_tail_hilbert_page(name):
+    """96x96 Hilbert-page shapes: 2,304 tiles on 1,024 resident workgroups
+    leave a last round of 256, split four ways (correct, though slower here
+    than unsplit: the benchmark launch does not take it)."""
+    _run(W.HILBERT_PAGE[name], split_tail=True)
 
 
 def test_split_tail_workspace_and_permute_passes():
@@ -196,9 +206,17 @@ def test_split_tail_workspace_and_permute_passes():
     both = int(L.na_forward_workspace_bytes(plan._h, 1, 2,
                                             na.NA_FWD_PERMUTE_PASSES | na.NA_FWD_SPLIT_TAIL))
     assert both == perm + one
-    # no split mode at 256-query tiles: the flag costs nothing there
-    plan256 = na.Plan(wl, q_block=256)
-    assert int(L.na_forward_workspace_bytes(plan256._h, 1, 2, na.NA_FWD_SPLIT_TAIL)) == 0
+    # no split with the fixed-fusion bias, nor with the separate softmax's
+    # partner branch fused into the 32-query-per-wave kernels: the flag costs
+    # nothing there
+    for mode, qb in (("fixed_fusion", 256), ("separate", 128)):
+        pw = W.scaled(W.CONFIGS["causal1d_bf16"], name="split_" + mode, H=1, D=64, grid=[500],
+                      pattern=dict(kind="band", left=40, right=0, skip=17, skip_mode=mode,
+                                   skip_prior=0.6))
+        pp = na.Plan(pw, q_block=qb)
+        assert int(L.na_forward_workspace_bytes(pp._h, 1, 1, na.NA_FWD_SPLIT_TAIL)) == 0
+        assert pp.stats["resident_workgroups"] == 0
+        _run(pw, q_block=qb, split_tail=True)
     _run(wl, q_block=384, permute_passes=True, split_tail=True)
     _run(wl, q_block=256, split_tail=True)
 
