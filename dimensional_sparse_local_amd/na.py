@@ -201,11 +201,14 @@ def forward_launch(w: dict) -> tuple[dict, int, bool]:
     """(kernel-side workload, query tile, split tail) for the forward pass
     alone, the fastest measured launch of each shape:
 
-    * bf16, head_dim 128, no fixed-fusion bias: 384-query tiles (the 16x16x32
-      MFMA kernel, 48 queries per wave): each staged K/V tile serves 1.5x the
-      queries of a 256-query tile, on full and partial tile pairs alike; with
-      the split tail, so that a last round of workgroups that would leave
-      most compute units idle is spread over all of them;
+    * bf16, head_dim 128, no fixed-fusion bias: the 16x16x32 MFMA kernel with
+      48 queries per wave, at 384-query tiles (8 waves: each staged K/V tile
+      serves 1.5x the queries of a 256-query tile) unless the tile map's
+      useful fraction there is more than 2 points below that at 192-query
+      tiles (4 waves, two workgroups per CU), as on the 1-D causal window
+      (0.915 against 0.955: 1.93 ms at 192 against 2.00 at 384, one box);
+      with the split tail, so that a last round of workgroups that would
+      leave most compute units idle is spread over all of them;
     * bf16, head_dim 64, 2-D neighbourhood or slide window in row-major order:
       8x8 patch order inside the kernel (q, k, v, out stay row-major) makes the
       visited tile pairs denser, and 64-query tiles give the short walks more
@@ -220,7 +223,9 @@ def forward_launch(w: dict) -> tuple[dict, int, bool]:
     pat = w["pattern"]
     bias = pat.get("skip", 0) > 0 and pat.get("skip_mode", "union") == "fixed_fusion"
     if w.get("dtype", "bf16") == "bf16" and int(w["D"]) == 128 and not bias:
-        return w, 384, True
+        u384 = Plan(w, host_only=True, q_block=384).speedup_bounds()["useful_fraction"]
+        u192 = Plan(w, host_only=True, q_block=192).speedup_bounds()["useful_fraction"]
+        return w, (384 if u384 >= u192 - 0.02 else 192), True
     if (w.get("dtype", "bf16") == "bf16" and int(w["D"]) == 64
             and w.get("order", "row_major") == "row_major" and len(w["grid"]) == 2
             and pat["kind"] in ("na", "sa")):
