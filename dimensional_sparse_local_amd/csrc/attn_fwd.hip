@@ -671,13 +671,28 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     // One K/V tile; mid() runs once the first half's scores are in registers
     // (the walk issues the next tile's DMA there, so its LDS writes overlap
     // the softmax and P.V products rather than this tile's K reads).
+    //
+    // With four waves (192-query tiles), a wave skips a half of a partial tile
+    // whose 32 keys none of its queries attends (bit hs of `live`); at eight
+    // waves the same test measured slower on full-tile maps and is compiled
+    // out.
     auto compute = [&](NaEntry entry, const u32x2* ml, const uint16_t* kl, const uint16_t* vl,
                        auto mid) {
+        uint32_t live = 3u;
+        if (NW == 4 && entry.mask >= 0) {
+            u32x2 any = ml[wave * (16 * QBN) + q16];
+#pragma unroll
+            for (int qb = 1; qb < QBN; ++qb) any |= ml[wave * (16 * QBN) + 16 * qb + q16];
+            live = (__builtin_amdgcn_ballot_w64(any[0] != 0u) ? 1u : 0u) |
+                   (__builtin_amdgcn_ballot_w64(any[1] != 0u) ? 2u : 0u);
+        }
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {   // two 32-key halves of the tile
+            const bool run = (live >> hs) & 1u;
             f32x4 s[2][QBN];
-            scores(hs, entry, ml, kl, s);
+            if (run) scores(hs, entry, ml, kl, s);
             if (hs == 0) mid();
+            if (!run) continue;
 
             // online softmax against each row's reference maximum, which moves
             // only for a row with none yet or a lane sum past 2^kSumLog2 (the
