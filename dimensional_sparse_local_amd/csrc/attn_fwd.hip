@@ -1008,28 +1008,39 @@ bool na_attn_supported(int dtype, int head_dim, int q_block, int kv_block, bool 
     return false;
 }
 
+namespace {
+
+// The kernel (and its block size) of a launch that has the split-walk mode,
+// or false.
+bool split_kernel(int dtype, int head_dim, int q_block, bool fusion, const void** fn, int* threads) {
+    if (dtype != NA_BF16 || fusion) return false;
+    if (head_dim == 64 && q_block == 64)
+        *fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 2>), *threads = 128;
+    else if (head_dim == 64 && q_block == 128)
+        *fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 4>), *threads = 256;
+    else if (head_dim == 64 && q_block == 256)
+        *fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 8>), *threads = 512;
+    else if (head_dim == 128 && q_block == 128)
+        *fn = reinterpret_cast<const void*>(&attn_fwd_bf16<128, 4>), *threads = 256;
+    else if (head_dim == 128 && q_block == 256)
+        *fn = reinterpret_cast<const void*>(&attn_fwd_bf16<128, 8>), *threads = 512;
+    else if (head_dim == 128 && q_block == 384)
+        *fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<128, 8>), *threads = 512;
+    else if (head_dim == 128 && q_block == 192)
+        *fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<128, 4>), *threads = 256;
+    else if (head_dim == 64 && q_block == 192)
+        *fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<64, 4>), *threads = 256;
+    else
+        return false;
+    return true;
+}
+
+}  // namespace
+
 int na_attn_split_capacity(int dtype, int head_dim, int q_block, bool fusion) {
-    if (dtype != NA_BF16 || fusion) return 0;
     const void* fn = nullptr;
     int threads = 0;
-    if (head_dim == 64 && q_block == 64)
-        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 2>), threads = 128;
-    else if (head_dim == 64 && q_block == 128)
-        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 4>), threads = 256;
-    else if (head_dim == 64 && q_block == 256)
-        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<64, 8>), threads = 512;
-    else if (head_dim == 128 && q_block == 128)
-        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<128, 4>), threads = 256;
-    else if (head_dim == 128 && q_block == 256)
-        fn = reinterpret_cast<const void*>(&attn_fwd_bf16<128, 8>), threads = 512;
-    else if (head_dim == 128 && q_block == 384)
-        fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<128, 8>), threads = 512;
-    else if (head_dim == 128 && q_block == 192)
-        fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<128, 4>), threads = 256;
-    else if (head_dim == 64 && q_block == 192)
-        fn = reinterpret_cast<const void*>(&attn_fwd_bf16_m16<64, 4>), threads = 256;
-    else
-        return 0;
+    if (!split_kernel(dtype, head_dim, q_block, fusion, &fn, &threads)) return 0;
     int per_cu = 0, dev = -1, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess ||
         hipGetDevice(&dev) != hipSuccess ||
@@ -1045,7 +1056,10 @@ int na_attn_launch(const NaAttnParams& p, int dtype, int head_dim, int q_block, 
     const dim3 grid((unsigned)(p.n_main + (int64_t)(p.n_wg - p.n_main) * p.n_split));
     const bool split = p.n_main < p.n_wg;
     const dim3 cgrid((unsigned)(((int64_t)(p.n_wg - p.n_main) * q_block * (head_dim / 4) + 255) / 256));
-    if (split && (na_attn_split_capacity(dtype, head_dim, q_block, fusion) == 0 || p.sep_skip > 0))
+    const void* split_fn = nullptr;
+    int split_threads = 0;
+    if (split && (!split_kernel(dtype, head_dim, q_block, fusion, &split_fn, &split_threads) ||
+                  p.sep_skip > 0))
         return (int)hipErrorInvalidValue;   // no shares with the bias or the fused partner branch
     if (fusion) {
         if (head_dim == 64 && q_block == 64)
