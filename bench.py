@@ -136,6 +136,11 @@ def main():
                          "patch order and 64 at head_dim 64 for 2-D windows in row-major order), "
                          "the backward pass the library default")
     ap.add_argument("--permute-passes", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph and time its replays (no host "
+                         "launch between steps; measured slower than direct launches for these "
+                         "one- or two-kernel steps, e.g. 38.3 against 32.6 us on the 64x64 "
+                         "neighbourhood: the direct launches are not host-bound)")
     ap.add_argument("--no-split-tail", action="store_true",
                     help="run the forward without NA_FWD_SPLIT_TAIL even where its launch "
                          "takes it")
@@ -257,6 +262,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        # one step captured into a HIP graph and replayed: no host launch
+        # cost between steps (the launches of a step are the same kernels)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
     log("bench: warmup done")
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -371,6 +393,7 @@ def main():
                    "effective_flops_per_step": flops,
                    "pct_of_peak": round(100.0 * tflops / peak, 2),
                    "permute_passes": bool(args.permute_passes), "split_tail": split,
+                   "graph": bool(args.graph),
                    "pass": args.which,
                    "internal_order": ({k: kernel_wl[k] for k in ("order", "tile")} if internal
                                       else {"order": wl["order"]})},
