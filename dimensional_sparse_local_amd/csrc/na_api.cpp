@@ -7,6 +7,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <chrono>
+#include <cstdlib>
 #include <cstring>
 #include <limits>
 #include <new>
@@ -15,6 +17,16 @@
 
 namespace {
 thread_local char g_err[512] = "";
+
+// NA_LOG=1 prints each plan's statistics to stderr when it is created;
+// NA_LOG=2 also prints every forward launch's grid and split.  Read once.
+int log_level() {
+    static const int level = [] {
+        const char* v = std::getenv("NA_LOG");
+        return v ? std::atoi(v) : 0;
+    }();
+    return level;
+}
 
 const char* hip_err(hipError_t e) { return hipGetErrorString(e); }
 
@@ -160,6 +172,7 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
         na_set_error("unknown plan flags 0x%x", flags);
         return NA_ERR_INVALID_ARG;
     }
+    const auto t_start = std::chrono::steady_clock::now();
     na_plan_s* p = new (std::nothrow) na_plan_s();
     if (!p) {
         na_set_error("host allocation failed");
@@ -216,6 +229,22 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
     }
     for (size_t t = 0; t + 1 < p->row_ptr.size(); ++t)
         p->max_row_len = std::max(p->max_row_len, p->row_ptr[t + 1] - p->row_ptr[t]);
+    if (log_level() >= 1) {
+        const double ms =
+            std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start)
+                .count();
+        const na_plan_stats& st = p->stats;
+        std::fprintf(stderr,
+                     "na: plan N=%lld order=%d head_dim=%d dtype=%d q_block=%lld kv_block=%lld "
+                     "tiles=%lldx%lld empty=%lld partial=%lld full=%lld masks=%lld "
+                     "pairs_per_head=%lld max_row=%d resident_workgroups=%lld %s %.2f ms\n",
+                     (long long)st.n_tokens, p->desc.order, p->desc.head_dim, p->desc.dtype,
+                     (long long)st.q_block, (long long)st.kv_block, (long long)st.n_q_tiles,
+                     (long long)st.n_kv_tiles, (long long)st.n_empty, (long long)st.n_partial,
+                     (long long)st.n_full, (long long)p->n_masks, (long long)st.attended_pairs,
+                     p->max_row_len, (long long)st.resident_workgroups,
+                     p->on_device ? "device" : "host-only", ms);
+    }
     *out = p;
     return NA_OK;
 }
@@ -378,6 +407,12 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
         if (n_split > 1) n_main = n_wg - r;
     }
 
+    if (log_level() >= 2)
+        std::fprintf(stderr,
+                     "na: forward B=%lld H=%lld q_block=%d workgroups=%lld whole=%lld shares=%lld "
+                     "(split %lld) flags=0x%x\n",
+                     (long long)B, (long long)H, p->desc.q_block, (long long)n_wg, (long long)n_main,
+                     (long long)((n_wg - n_main) * n_split), (long long)n_split, flags);
     NaAttnParams a{};
     a.n_tokens = (int32_t)p->n_tokens;
     a.heads = (int32_t)H;

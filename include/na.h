@@ -212,7 +212,10 @@ typedef struct na_plan_s* na_plan_t;
  * Returns NA_ERR_INVALID_ARG for a malformed descriptor, NA_ERR_UNSUPPORTED for
  * a Hilbert order on a grid that is not 2-D, NA_ERR_OUT_OF_MEMORY or
  * NA_ERR_DEVICE if a host or device allocation or upload fails (nothing is
- * leaked). */
+ * leaked).  With the environment variable NA_LOG=1 (read once per process)
+ * each created plan's statistics and build time go to stderr as one line;
+ * NA_LOG=2 adds one line per na_forward launch (grid, whole tiles, split
+ * shares).  Otherwise the library prints nothing. */
 na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* plan);
 
 /* Release a plan (host and device memory).  The caller must first make sure

@@ -161,3 +161,25 @@ def test_split_tail_flag_on_host_only_plan():
     assert int(L.na_forward_workspace_bytes(plan._h, 1, 2, na.NA_FWD_SPLIT_TAIL)) == 0
     st = L.na_forward(plan._h, 1, 2, None, None, None, None, None, 0.1, 4, None, 0, None)
     assert st in (na.NA_ERR_INVALID_ARG, na.NA_ERR_PLAN_MISMATCH)
+
+
+def test_na_log_prints_plan_statistics():
+    """NA_LOG=1 makes plan creation print one line of tile-map statistics to
+    stderr; without it the library prints nothing."""
+    import subprocess
+    import sys
+
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from dimensional_sparse_local_amd import na, workloads as W\n"
+            "na.Plan(W.CONFIGS['na2d_fp32'], host_only=True)\n") % ROOT
+    env = dict(os.environ)
+    env.pop("NA_LOG", None)
+    quiet = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True)
+    assert quiet.returncode == 0, quiet.stderr
+    assert "na: plan" not in quiet.stderr
+    env["NA_LOG"] = "1"
+    loud = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True)
+    assert loud.returncode == 0, loud.stderr
+    lines = [l for l in loud.stderr.splitlines() if l.startswith("na: plan")]
+    assert len(lines) == 1
+    assert "N=64 " in lines[0] and "pairs_per_head=576 " in lines[0] and "host-only" in lines[0]
