@@ -24,11 +24,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 # instructions (infinities, used for masked scores, are still honoured).
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
                 "-packed-fp32-ops", "-fno-honor-nans"]
-# Per-source extras.  The key-major gradient kernel runs one wave per SIMD with
-# up to 512 registers: its MFMA accumulators stay in ordinary vector registers
-# (the softmax reads them directly) and the accumulation registers serve as
-# spill space.
-SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extras (none at present).
+SOURCE_FLAGS = {}
 
 
 def _run(cmd, verbose):
