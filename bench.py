@@ -62,8 +62,9 @@ def _stats(xs):
 def kernel_signature() -> str:
     """sha256[:16] of the source of the 48-query-per-wave forward kernel and
     its combine kernel (the part of attn_fwd.hip from the 16x16x32 helpers to
-    the fp32 kernel) followed by attn_common.h: the code the committed
-    traffic counters were taken on."""
+    the fp32 kernel), attn_common.h and the planner (plan.cpp: the walk order
+    of each tile row and the dispatch order of the tiles): the code the
+    committed traffic counters were taken on."""
     import hashlib
 
     csrc = os.path.join(ROOT, "dimensional_sparse_local_amd", "csrc")
@@ -73,8 +74,9 @@ def kernel_signature() -> str:
     end = text.index(b"// fp32: one wave, 32 queries", start)
     h = hashlib.sha256()
     h.update(text[start:end])
-    with open(os.path.join(csrc, "attn_common.h"), "rb") as f:
-        h.update(f.read())
+    for name in ("attn_common.h", "plan.cpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -130,6 +130,16 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// Logical tile index -> query tile of its (batch, head), in ascending order
+// or (desc) descending.  On a causal window the tiles at the start of the
+// sequence have the shortest walks; taking them last lets them fill the final
+// round of workgroups instead of leaving compute units idle behind
+// full-length ones (longest first, as in list scheduling).
+__device__ __forceinline__ int tile_of(int wg, int n_q_tiles, int desc) {
+    const int t = wg % n_q_tiles;
+    return desc ? n_q_tiles - 1 - t : t;
+}
+
 // Workgroup index -> logical tile index.  Workgroups are dispatched to the 8
 // XCDs round-robin; give each XCD one contiguous range of logical tiles
 // (consecutive query tiles of one head) so that the tiles sharing key/value

@@ -81,7 +81,7 @@ void attn_fwd_bf16(NaAttnParams p) {
     const bool part_mode = (int)blockIdx.x >= p.n_main;
     const int part = (int)blockIdx.x - p.n_main;
     const int wg = part_mode ? p.n_main + part / p.n_split : xcd_remap(blockIdx.x, p.n_main);
-    const int qt = wg % p.n_q_tiles;
+    const int qt = tile_of(wg, p.n_q_tiles, p.q_desc);
     const int bh = wg / p.n_q_tiles;
     const int b = bh / p.heads, h = bh % p.heads;
     const int N = p.n_tokens;
@@ -536,7 +536,7 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     const bool part_mode = (int)blockIdx.x >= p.n_main;
     const int part = (int)blockIdx.x - p.n_main;
     const int wg = part_mode ? p.n_main + part / p.n_split : xcd_remap(blockIdx.x, p.n_main);
-    const int qt = wg % p.n_q_tiles;
+    const int qt = tile_of(wg, p.n_q_tiles, p.q_desc);
     const int bh = wg / p.n_q_tiles;
     const int b = bh / p.heads, h = bh % p.heads;
     const int N = p.n_tokens;
@@ -838,7 +838,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(NaAttnParams p) {
     if (gr >= (p.n_wg - p.n_main) * QB) return;
     const int tt = gr / QB, row = gr % QB;
     const int wg = p.n_main + tt;
-    const int qt = wg % p.n_q_tiles, bh = wg / p.n_q_tiles;
+    const int qt = tile_of(wg, p.n_q_tiles, p.q_desc), bh = wg / p.n_q_tiles;
     const int b = bh / p.heads, h = bh % p.heads;
     const int qpos = qt * QB + row;
     if (qpos >= p.n_tokens) return;

@@ -237,13 +237,13 @@ na_status na_plan_create(const na_plan_desc* desc, uint32_t flags, na_plan_t* ou
         std::fprintf(stderr,
                      "na: plan N=%lld order=%d head_dim=%d dtype=%d q_block=%lld kv_block=%lld "
                      "tiles=%lldx%lld empty=%lld partial=%lld full=%lld masks=%lld "
-                     "pairs_per_head=%lld max_row=%d resident_workgroups=%lld %s %.2f ms\n",
+                     "pairs_per_head=%lld max_row=%d resident_workgroups=%lld tile_order=%s %s %.2f ms\n",
                      (long long)st.n_tokens, p->desc.order, p->desc.head_dim, p->desc.dtype,
                      (long long)st.q_block, (long long)st.kv_block, (long long)st.n_q_tiles,
                      (long long)st.n_kv_tiles, (long long)st.n_empty, (long long)st.n_partial,
                      (long long)st.n_full, (long long)p->n_masks, (long long)st.attended_pairs,
                      p->max_row_len, (long long)st.resident_workgroups,
-                     p->on_device ? "device" : "host-only", ms);
+                     p->q_desc ? "descending" : "ascending", p->on_device ? "device" : "host-only", ms);
     }
     *out = p;
     return NA_OK;
@@ -420,6 +420,7 @@ na_status na_forward(na_plan_t p, int64_t B, int64_t H, const na_tensor* q, cons
     a.n_wg = (int32_t)n_wg;
     a.n_main = (int32_t)n_main;
     a.n_split = (int32_t)n_split;
+    a.q_desc = p->q_desc ? 1 : 0;
     if (n_split > 1) {
         char* sw = (char*)workspace + permute_ws_bytes(p, B, H, flags);
         const size_t rows = (size_t)(kShareRounds * p->split_capacity) * (size_t)d.q_block;

@@ -74,6 +74,10 @@ struct na_plan_s {
     // (compute units x workgroups per unit), for kernels with a split-walk
     // mode; 0 otherwise or for host-only plans
     int32_t split_capacity = 0;
+    // dispatch the query tiles of each (batch, head) in descending order: set
+    // for one-dimensional maps whose walks grow along the sequence (causal
+    // windows), so that the short walks at its start come last
+    bool q_desc = false;
 
     // device copies (null when host-only or not needed)
     bool on_device = false;
@@ -139,6 +143,8 @@ struct NaAttnParams {
     int32_t n_split;
     float* part_o;
     float* part_ml;
+    // 1: query tiles of each (batch, head) in descending order (tile_of)
+    int32_t q_desc;
 };
 
 // Gradient launch parameters (attn_bwd.hip).  Tensors as in NaAttnParams;

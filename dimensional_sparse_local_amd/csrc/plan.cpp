@@ -520,6 +520,23 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
     }
     p->n_masks = (int64_t)seen.size();
 
+    // ---- walk order inside a row -----------------------------------------------
+    // A row whose key/value tiles are consecutive (bands, causal windows) is
+    // stored rotated: it starts at its tile whose index is a multiple of the
+    // row length and wraps around.  Neighbouring query tiles, whose rows
+    // overlap, then stage the same key/value tile at the same step of their
+    // walks, so workgroups running at the same time share it in L2.  The
+    // kernels' online softmax takes a row's tiles in any order; rows of other
+    // shapes stay ascending.
+    for (int64_t qt = 0; qt < nqt; ++qt) {
+        const int32_t r0 = p->row_ptr[qt], r1 = p->row_ptr[qt + 1];
+        const int32_t len = r1 - r0;
+        if (len < 2 || p->entries[r1 - 1].kt - p->entries[r0].kt != len - 1) continue;
+        const int32_t j0 = (len - p->entries[r0].kt % len) % len;
+        std::rotate(p->entries.begin() + r0, p->entries.begin() + r0 + j0, p->entries.begin() + r1);
+        std::rotate(p->entry_cls.begin() + r0, p->entry_cls.begin() + r0 + j0, p->entry_cls.begin() + r1);
+    }
+
     // ---- the same map by key/value tile --------------------------------------
     p->t_row_ptr.assign(nkt + 1, 0);
     for (const NaEntry& e : p->entries) ++p->t_row_ptr[e.kt + 1];
@@ -552,6 +569,13 @@ na_status na_plan_build_host(const na_plan_desc* in, na_plan_s* p) {
             p->p_row_ptr[g + 1] = (int32_t)p->p_entries.size();
         }
     }
+    // ---- dispatch order of the query tiles ----------------------------------------
+    // A one-dimensional map whose first walk is shorter than its last (a causal
+    // window: the walks grow from the start of the sequence) runs its query
+    // tiles in descending order, longest walks first.  Maps in more dimensions
+    // keep ascending order, which measured faster on the tiled windows.
+    p->q_desc = p->pdims == 1 && nqt > 1 &&
+                p->row_ptr[1] - p->row_ptr[0] < p->row_ptr[nqt] - p->row_ptr[nqt - 1];
     p->stats.n_tokens = N;
     p->stats.q_block = qb;
     p->stats.kv_block = kb;

@@ -183,3 +183,26 @@ def test_na_log_prints_plan_statistics():
     lines = [l for l in loud.stderr.splitlines() if l.startswith("na: plan")]
     assert len(lines) == 1
     assert "N=64 " in lines[0] and "pairs_per_head=576 " in lines[0] and "host-only" in lines[0]
+
+
+def test_tile_order_of_causal_and_other_maps():
+    """A one-dimensional map whose walks grow along the sequence (a causal
+    window) dispatches its query tiles longest first; a two-sided band and a
+    2-D neighbourhood keep ascending order (the plan line of NA_LOG=1)."""
+    import subprocess
+    import sys
+
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from dimensional_sparse_local_amd import na, workloads as W\n"
+            "c = W.CONFIGS['causal1d_bf16']\n"
+            "na.Plan(W.scaled(c, H=2, grid=[3000], pattern=dict(kind='band', left=600, right=0)), host_only=True)\n"
+            "na.Plan(W.scaled(c, H=2, grid=[3000], pattern=dict(kind='band', left=600, right=600)), host_only=True)\n"
+            "na.Plan(W.CONFIGS['na2d_fp32'], host_only=True)\n") % ROOT
+    env = dict(os.environ, NA_LOG="1")
+    run = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True)
+    assert run.returncode == 0, run.stderr
+    lines = [l for l in run.stderr.splitlines() if l.startswith("na: plan")]
+    assert len(lines) == 3
+    assert "tile_order=descending " in lines[0]
+    assert "tile_order=ascending " in lines[1]
+    assert "tile_order=ascending " in lines[2]
