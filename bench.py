@@ -130,7 +130,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: as many as fill 1 s, at least 5: the "
+                         "clock ramps up over the first tens of milliseconds of load, which "
+                         "a sub-millisecond step would otherwise time)")
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--q-block", type=int, default=0,
                     help="query tile; 0 = the forward pass takes the launch of "
@@ -261,8 +264,17 @@ def main():
         def step():
             plan.backward(q, k, v, out, lse, dout, scale=scale, grads=grads, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        args.warmup = 0
+        t_warm = time.perf_counter()
+        while args.warmup < 5 or time.perf_counter() - t_warm < 1.0:
+            step()
+            args.warmup += 1
+            if args.warmup % 8 == 0:
+                torch.cuda.synchronize()
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
     if args.graph:
         # one step captured into a HIP graph and replayed: no host launch
