@@ -59,9 +59,12 @@ __device__ __forceinline__ NaEntry load_entry(const NaEntry* e) {
 template <bool BIAS> struct MaskRow { using T = u32x2; };
 template <> struct MaskRow<true> { using T = u32x4; };
 
-// Keep score x when bit `bit` of word w is set, else -inf.
+// Keep score x when bit `bit` of word w is set, else -inf: the bit, extracted
+// sign-extended, selects between the two bit patterns (two VALU instructions,
+// no compare-and-select through VCC).
 __device__ __forceinline__ float keep_if(uint32_t w, int bit, float x) {
-    return (w >> bit) & 1u ? x : kNegInf;
+    const uint32_t m = (uint32_t)((int32_t)(w << (31 - bit)) >> 31);
+    return __builtin_bit_cast(float, (m & __builtin_bit_cast(uint32_t, x)) | (~m & 0xff800000u));
 }
 
 // Online softmax in the log2 domain against a reference maximum per row: the

@@ -258,15 +258,22 @@ void attn_fwd_bf16(NaAttnParams p) {
         // Online softmax against a reference maximum that moves only when it
         // must: the probabilities are taken against the row's current
         // reference, and the exact tile maximum is formed only if a row has no
-        // reference yet or a lane's sum of this tile's probabilities (which
-        // bounds each of them) passes 2^kSumLog2.  Then the wave recomputes the
-        // scores and moves every row's reference to max(reference, tile
+        // reference yet (taken from these scores) or a lane's sum of this
+        // tile's probabilities (which bounds each of them) passes 2^kSumLog2
+        // (the wave then recomputes the scores the exponentials overwrote).
+        // The wave moves every row's reference to max(reference, tile
         // maximum), rescaling O and l; the result is exact after the final
         // division by l either way.
-        float ts = probs(s, live);
-        const bool redo = m_ref == kNegInf || !(ts <= kSumMax);
-        if (__builtin_amdgcn_ballot_w64(redo)) {
-            scores(entry, ml, kl, s);
+        float ts = 0.f;
+        bool need_max = __builtin_amdgcn_ballot_w64(m_ref == kNegInf) != 0;
+        if (!need_max) {
+            ts = probs(s, live);
+            if (__builtin_amdgcn_ballot_w64(!(ts <= kSumMax))) {
+                need_max = true;
+                scores(entry, ml, kl, s);
+            }
+        }
+        if (need_max) {
             float mx = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
