@@ -149,6 +149,11 @@ def main():
     ap.add_argument("--no-split-tail", action="store_true",
                     help="run the forward without NA_FWD_SPLIT_TAIL even where its launch "
                          "takes it")
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="also time the Hilbert page's protocol after the timed steps: this many "
+                         "rounds of 100 iterations, each after 25 untimed ones (a quarter of "
+                         "the round), reported as the median, min and max of the rounds' mean "
+                         "step times under \"rounds_ms\" (10 on the page; 0 = off)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=("forward", "backward", "permute"),
@@ -312,6 +317,26 @@ def main():
     step_stats = _stats(per_step)
     log("bench: %.3f ms/step (median %.3f, min %.3f, max %.3f)"
         % (ms, step_stats["median"], step_stats["min"], step_stats["max"]))
+    rounds_stats = None
+    if args.rounds > 0:
+        # "Hilbert-Guided Sparse Local Attention", Methodology in Plain English:
+        # the median over repeated rounds of 100 iterations, a quarter of each
+        # round run first as warm-up
+        round_ms = []
+        for _ in range(args.rounds):
+            for _ in range(25):
+                step()
+            r0 = torch.cuda.Event(enable_timing=True)
+            r1 = torch.cuda.Event(enable_timing=True)
+            r0.record(stream)
+            for _ in range(100):
+                step()
+            r1.record(stream)
+            torch.cuda.synchronize()
+            round_ms.append(r0.elapsed_time(r1) / 100)
+        rounds_stats = dict(_stats(round_ms), rounds=args.rounds, iterations=100, warmup=25)
+        log("bench: rounds of 100: median %.4f ms (min %.4f, max %.4f)"
+            % (rounds_stats["median"], rounds_stats["min"], rounds_stats["max"]))
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl["dtype"]]
     # Algorithmic HBM bytes per step: every tensor read or written once
@@ -395,6 +420,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "step_ms": step_stats,
+        **({"rounds_ms": rounds_stats} if rounds_stats else {}),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
