@@ -500,7 +500,14 @@ void attn_bwd_dkdv(NaBwdParams p) {
         }
     };
     auto aux_store = [&](Step st, float lr, float dl, u32x4 mw, float* aux) {
-        const int t = lane & 31;
+        // The lane index is passed through an empty asm statement so that the
+        // compiler recomputes this step's LDS addresses (a few VALU
+        // instructions) instead of keeping them across the walk: at 256
+        // registers they would be spilled, and reloading a spill is a vector
+        // memory access whose wait would also wait for the step's DMA.
+        int lane_r = lane;
+        asm volatile("" : "+v"(lane_r));
+        const int t = lane_r & 31;
         const int a = t >> 4, rem = t & 15;
         const int pos = 16 * (rem & 1) + 8 * a + 4 * ((rem >> 1) & 1) + (rem >> 2);
         const bool valid = aux_valid(st);
@@ -509,11 +516,11 @@ void attn_bwd_dkdv(NaBwdParams p) {
             aux[QS + pos] = valid ? dl : 0.f;
         }
         // a tile attended without a mask keeps every bit
-        ((uint32_t*)aux)[2 * QS + lane] = st.mask0 == -1 ? ~0u : mw[0];
-        ((uint32_t*)aux)[4 * QS + lane] = st.mask1 == -1 ? ~0u : mw[1];
+        ((uint32_t*)aux)[2 * QS + lane_r] = st.mask0 == -1 ? ~0u : mw[0];
+        ((uint32_t*)aux)[4 * QS + lane_r] = st.mask1 == -1 ? ~0u : mw[1];
         if constexpr (BIAS) {
-            ((uint32_t*)aux)[6 * QS + lane] = mw[2];
-            ((uint32_t*)aux)[8 * QS + lane] = mw[3];
+            ((uint32_t*)aux)[6 * QS + lane_r] = mw[2];
+            ((uint32_t*)aux)[8 * QS + lane_r] = mw[3];
         }
     };
 
