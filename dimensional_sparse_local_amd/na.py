@@ -206,7 +206,7 @@ def forward_launch(w: dict) -> tuple[dict, int, bool]:
       serves 1.5x the queries of a 256-query tile) unless the tile map's
       useful fraction there is more than 2 points below that at 192-query
       tiles (4 waves, two workgroups per CU), as on the 1-D causal window
-      (0.915 against 0.955: 1.93 ms at 192 against 2.00 at 384, one box);
+      (0.915 against 0.955: 1.86 ms at 192 against 1.93 at 384, one box);
       with the split tail, so that a last round of workgroups that would
       leave most compute units idle is spread over all of them;
     * bf16, head_dim 64, 2-D neighbourhood or slide window in row-major order:
