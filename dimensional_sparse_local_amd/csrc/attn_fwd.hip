@@ -517,10 +517,18 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     constexpr int QBN = 3;                       // 16-query blocks per wave
     constexpr int QB = 16 * QBN * NW;            // 192 or 384
     constexpr int KV = NA_KV_BLOCK_BF16;
-    constexpr int ROW = D + 8;
-    constexpr int CS = D / 8 + 1;
+    // K and V tiles in LDS.  At D = 128 a row is 16 chunks of 16 bytes stored
+    // unpadded, chunk j of row r at position j ^ (r % 16) of the row: the K
+    // reads of a 16-lane phase (16 rows, one chunk each) and the transpose
+    // reads of V (8 rows, 32 bytes each) then fall on distinct banks, and a
+    // tile is 16 DMA blocks, two or four per wave.  Otherwise (D = 64) rows
+    // are padded by one chunk (the pad slot re-reads chunk 0 and is never
+    // read back).
+    constexpr bool SWZ = D == 128;
+    constexpr int ROW = SWZ ? D : D + 8;
+    constexpr int CS = SWZ ? D / 8 : D / 8 + 1;   // 16-byte slots per row
     constexpr int TILE = KV * ROW;
-    constexpr int NI = CS;
+    constexpr int NI = KV * CS / 64;              // 1 KB DMA blocks per tile
     constexpr int IPW = (NI + NW - 1) / NW;
     constexpr int KS = D / 32;                   // QK reduction steps
     constexpr int DB = D / 16;                   // PV output blocks
@@ -574,8 +582,10 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
     // clamped to it (masked keys, probability exactly 0).
     auto dma_row = [&](int i) { return (64 * (wave + NW * i) + lane) / CS; };
     auto dma_cb = [&](int i) {
-        const uint32_t ch = (64 * (wave + NW * i) + lane) % CS;
-        return ch < CS - 1 ? 16u * ch : 0u;
+        const int slot = 64 * (wave + NW * i) + lane;
+        const uint32_t ch = (uint32_t)(slot % CS);
+        if constexpr (SWZ) return 16u * (ch ^ ((uint32_t)(slot / CS) & 15u));
+        else return ch < CS - 1 ? 16u * ch : 0u;
     };
     auto tokens = [&](NaEntry entry, int* tok) {
 #pragma unroll
@@ -617,7 +627,14 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
 
     const int pim = q16;   // A-operand row of this lane inside a 16-key block
     const int pi = 4 * (pim & 3) + 2 * ((pim >> 2) & 1) + (pim >> 3);
-    const int tr_base = (4 * (q16 >> 2) + cg) * ROW + 4 * (q16 & 3);
+    // element offsets inside a row: of this lane's K fragment for step ks (row
+    // 32*hs + 16*kb + pi), and of its V^T transpose read for output block db
+    // (row 32*hs + 16*j + vrow)
+    auto kcol = [&](int ks) { return SWZ ? 8 * ((4 * ks + g) ^ pi) : 32 * ks + 8 * g; };
+    const int vrow = 4 * (q16 >> 2) + cg;
+    auto vcol = [&](int db) {
+        return SWZ ? 8 * ((2 * db + ((q16 & 3) >> 1)) ^ vrow) + 4 * (q16 & 1) : 16 * db + 4 * (q16 & 3);
+    };
 
     // S^T blocks of one 32-key half: keys 32*hs + 16*kb .. +15, queries of
     // block qb; masked where the tile is partial (or runs past the last key).
@@ -629,15 +646,15 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
         {
             // k-step outer, one step of lookahead: fragments of both 16-key
             // blocks for step ks+1 load while the 6 MFMAs of step ks run
-            const uint16_t* kr = kl + (32 * hs + pi) * ROW + 8 * g;
-            bf16x8 a0 = *(const bf16x8*)(kr);
-            bf16x8 a1 = *(const bf16x8*)(kr + 16 * ROW);
+            const uint16_t* kr = kl + (32 * hs + pi) * ROW;
+            bf16x8 a0 = *(const bf16x8*)(kr + kcol(0));
+            bf16x8 a1 = *(const bf16x8*)(kr + 16 * ROW + kcol(0));
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 bf16x8 n0 = a0, n1 = a1;
                 if (ks + 1 < KS) {
-                    n0 = *(const bf16x8*)(kr + 32 * (ks + 1));
-                    n1 = *(const bf16x8*)(kr + 16 * ROW + 32 * (ks + 1));
+                    n0 = *(const bf16x8*)(kr + kcol(ks + 1));
+                    n1 = *(const bf16x8*)(kr + 16 * ROW + kcol(ks + 1));
                 }
 #pragma unroll
                 for (int qb = 0; qb < QBN; ++qb) {
@@ -740,11 +757,11 @@ void attn_fwd_bf16_m16(NaAttnParams p) {
             }
             // O^T += V^T P^T: the transpose reads give slot j' of group g the
             // row 32*hs + 4*j' + cg (first read) or + 16 (second read)
-            const uint16_t* vr = vl + tr_base + 32 * hs * ROW;
+            const uint16_t* vr = vl + (32 * hs + vrow) * ROW;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16x4 lo = lds_read_tr(vr + 16 * db);
-                const bf16x4 hi = lds_read_tr(vr + 16 * ROW + 16 * db);
+                const bf16x4 lo = lds_read_tr(vr + vcol(db));
+                const bf16x4 hi = lds_read_tr(vr + 16 * ROW + vcol(db));
                 const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int qb = 0; qb < QBN; ++qb)
