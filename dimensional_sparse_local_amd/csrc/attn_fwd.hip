@@ -496,8 +496,9 @@ void attn_fwd_bf16(NaAttnParams p) {
 // column l%16 and rows 4*(l/16) .. +3.  Within a 16-key block, MFMA row m is
 // fed by key pi(m) = 4*(m%4) + 2*(m/4 % 2) + m/8, so lane-group g holds keys
 // 4*i + cg with cg = 2*(g%2) + g/2: the rows of each V^T transpose read are
-// spaced two apart (conflict-free at the padded stride) and the K reads of a
-// 16-lane phase cover 16 distinct rows.
+// spaced two apart and the K reads of a 16-lane phase cover 16 distinct rows,
+// which keeps both on distinct banks, at the padded stride (D = 64) and with
+// the chunk permutation of the unpadded rows (D = 128).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float quad_max(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
